@@ -1,0 +1,113 @@
+"""Seeded synthetic attention inputs shared by the kernel tests, the bench and the oracle checks.
+
+This module only draws numbers.  It holds no attention arithmetic, so both the HIP path
+and the CPU oracle can consume its tensors without sharing any of the method's code.
+
+The workloads are synthetic stand-ins for the attention shapes the pages talk about
+(long-context causal self-attention and the softmax over a triangular score matrix,
+"Show HN: Flash Attention in ~100 lines of CUDA" and the FlashAttention-3 discussion on
+Hacker News).  The pages print no dataset, so every tensor is i.i.d. noise with the stated
+distribution, drawn in float32 from a seeded CPU generator and rounded to bfloat16 with
+round-to-nearest-even.  Draw order is always Q, then K, then V from one generator.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import torch
+
+__all__ = ["Workload", "CONFIGS", "by_name", "fp32_scale", "make_inputs", "sample_rows"]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    seed: int
+    # "normal": Q, K, V ~ N(0, 1).
+    # "stress": Q, K ~ N(0, 2^2) (large logits), V ~ U(-1, 1).
+    dist: str = "normal"
+    # None: compare every output row with the oracle.  An int: compare that many seeded
+    # sampled (b, h, i) rows.
+    oracle_rows: int | None = None
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+
+# The five seeded configurations; C1 and C2 run both with and without the causal mask.
+CONFIGS = [
+    Workload("C1-nc", 1, 1, 128, 64, False, 101),
+    Workload("C1-c", 1, 1, 128, 64, True, 101),
+    Workload("C2-nc", 4, 8, 1024, 64, False, 102),
+    Workload("C2-c", 4, 8, 1024, 64, True, 102),
+    Workload("C3", 2, 16, 4096, 128, True, 103),
+    Workload("C4", 1, 32, 16384, 128, True, 104, oracle_rows=256),
+    Workload("C5", 8, 16, 2048, 128, True, 105, dist="stress"),
+]
+
+
+def by_name(name: str) -> Workload:
+    for w in CONFIGS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def fp32_scale(d: int) -> float:
+    """1/sqrt(d) rounded to float32, returned as a Python float.
+
+    The library takes the softmax scale as a float32, so this is the exact value both the
+    kernel and the oracle use."""
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())
+
+
+def make_inputs(B: int, H: int, N: int, d: int, seed: int, dist: str = "normal"):
+    """Return bf16 CPU tensors q, k, v of shape [B, H, N, d], contiguous, d fastest."""
+    g = torch.Generator().manual_seed(seed)
+    shape = (B, H, N, d)
+    if dist == "normal":
+        q = torch.randn(shape, generator=g)
+        k = torch.randn(shape, generator=g)
+        v = torch.randn(shape, generator=g)
+    elif dist == "stress":
+        q = 2.0 * torch.randn(shape, generator=g)
+        k = 2.0 * torch.randn(shape, generator=g)
+        v = 2.0 * torch.rand(shape, generator=g) - 1.0
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    return (q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16))
+
+
+def make_workload_inputs(w: Workload):
+    return make_inputs(w.B, w.H, w.N, w.d, w.seed, w.dist)
+
+
+def sample_rows(B: int, H: int, N: int, count: int, seed: int) -> torch.Tensor:
+    """Distinct seeded (b, h, i) query rows, as an int64 tensor of shape [count, 3].
+
+    The edge rows i in {0, 1, 127, 128, N-1} of one seeded head are always included (those
+    that exist); the rest are drawn uniformly without replacement from all B*H*N rows."""
+    g = torch.Generator().manual_seed(seed + 1000)
+    total = B * H * N
+    count = min(count, total)
+    head = int(torch.randint(0, B * H, (1,), generator=g).item())
+    edge = sorted({i for i in (0, 1, 127, 128, N - 1) if 0 <= i < N})
+    chosen = [head * N + i for i in edge][:count]
+    taken = set(chosen)
+    perm = torch.randperm(total, generator=g)
+    for flat in perm.tolist():
+        if len(chosen) >= count:
+            break
+        if flat not in taken:
+            taken.add(flat)
+            chosen.append(flat)
+    flat = torch.tensor(chosen, dtype=torch.int64)
+    bh, i = flat // N, flat % N
+    return torch.stack([bh // H, bh % H, i], dim=1)

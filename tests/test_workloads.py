@@ -1,0 +1,49 @@
+"""The seeded input generator: determinism, dtypes, shapes and the sampled-row recipe."""
+import torch
+
+from io_aware_softmax_mifa_amd import workloads as W
+
+
+def test_make_inputs_deterministic_bf16():
+    a = W.make_inputs(1, 2, 33, 64, seed=7)
+    b = W.make_inputs(1, 2, 33, 64, seed=7)
+    c = W.make_inputs(1, 2, 33, 64, seed=8)
+    for x, y in zip(a, b):
+        assert x.dtype == torch.bfloat16 and x.shape == (1, 2, 33, 64) and x.is_contiguous()
+        assert torch.equal(x, y)
+    assert not torch.equal(a[0], c[0])
+    # Q, K and V are distinct draws from the one generator.
+    assert not torch.equal(a[0], a[1]) and not torch.equal(a[1], a[2])
+
+
+def test_stress_distribution_ranges():
+    q, k, v = W.make_inputs(2, 2, 256, 128, seed=5, dist="stress")
+    assert 1.7 < q.float().std().item() < 2.3 and 1.7 < k.float().std().item() < 2.3
+    assert v.float().abs().max().item() <= 1.0
+    assert 0.5 < v.float().std().item() * 3 ** 0.5 < 1.1  # U(-1, 1) has std 1/sqrt(3)
+
+
+def test_fp32_scale():
+    assert W.fp32_scale(64) == 0.125
+    s = W.fp32_scale(128)
+    assert s == float(torch.tensor(128 ** -0.5, dtype=torch.float32))
+
+
+def test_sample_rows_distinct_with_edges():
+    rows = W.sample_rows(1, 32, 16384, 256, seed=104)
+    assert rows.shape == (256, 3)
+    flat = [tuple(r) for r in rows.tolist()]
+    assert len(set(flat)) == 256
+    head = rows[0, :2].tolist()
+    edges = {r[2] for r in flat if list(r[:2]) == head}
+    assert {0, 1, 127, 128, 16383} <= edges
+    assert rows[:, 0].max() < 1 and rows[:, 1].max() < 32 and rows[:, 2].max() < 16384
+    assert torch.equal(rows, W.sample_rows(1, 32, 16384, 256, seed=104))
+
+
+def test_configs_table():
+    names = [w.name for w in W.CONFIGS]
+    assert names == ["C1-nc", "C1-c", "C2-nc", "C2-c", "C3", "C4", "C5"]
+    c4 = W.by_name("C4")
+    assert c4.shape == (1, 32, 16384, 128) and c4.causal and c4.oracle_rows == 256
+    assert W.by_name("C5").dist == "stress"

@@ -1,0 +1,138 @@
+"""Thin ctypes binding of libmifa (C ABI in include/mifa.h).
+
+Argument marshalling only: every step of attention runs in the HIP library.  torch supplies
+device memory and the current stream.  If the library is missing this module raises at import
+time; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmifa.so")
+
+MIFA_OK = 0
+STATUS_NAMES = {
+    0: "MIFA_OK",
+    1: "MIFA_ERR_NULL_POINTER",
+    2: "MIFA_ERR_BAD_SHAPE",
+    3: "MIFA_ERR_UNSUPPORTED_D",
+    4: "MIFA_ERR_MISALIGNED",
+    5: "MIFA_ERR_BAD_SCALE",
+    6: "MIFA_ERR_TOO_LARGE",
+    7: "MIFA_ERR_HIP",
+}
+EXPORTED = ("mifa_fwd", "mifa_status_string", "mifa_version", "mifa_last_hip_error")
+
+
+class MifaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"libmifa.so not found at {_LIB_PATH}; build it with "
+            "`python -m io_aware_softmax_mifa_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.mifa_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_float,
+                                                                             ctypes.c_void_p]
+    lib.mifa_fwd.restype = ctypes.c_int
+    lib.mifa_status_string.argtypes = [ctypes.c_int]
+    lib.mifa_status_string.restype = ctypes.c_char_p
+    lib.mifa_version.argtypes = []
+    lib.mifa_version.restype = ctypes.c_char_p
+    lib.mifa_last_hip_error.argtypes = []
+    lib.mifa_last_hip_error.restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def mifa_status_string(status: int) -> str:
+    return _lib.mifa_status_string(int(status)).decode()
+
+
+def mifa_version() -> str:
+    return _lib.mifa_version().decode()
+
+
+def mifa_last_hip_error() -> int:
+    return int(_lib.mifa_last_hip_error())
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def mifa_fwd_raw(q, k, v, o, lse, B, H, N, d, causal, scale, stream) -> int:
+    """Call the C entry point with raw integer pointers or tensors; returns the status code."""
+    return int(_lib.mifa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(N), int(d),
+                             1 if causal else 0, float(scale), stream or None))
+
+
+def mifa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> None:
+    """Same arguments as the C function; tensors or integer device pointers.  Raises MifaError."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = mifa_fwd_raw(q, k, v, o, lse, B, H, N, d, causal, scale, stream)
+    if st != MIFA_OK:
+        extra = f" (hipError {mifa_last_hip_error()})" if st == 7 else ""
+        raise MifaError(st, mifa_status_string(st) + extra)
+
+
+def _check(name, t, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, d]")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != shape:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale=None,
+              out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Exact attention forward.  q, k, v: bf16 [B, H, N, d] on the GPU (d = 64 or 128).
+
+    Returns (O float32 [B, H, N, d], LSE float32 [B, H, N]); both are allocated here unless
+    given.  The launch is asynchronous on torch's current stream."""
+    _check("q", q)
+    shape = tuple(q.shape)
+    _check("k", k, shape)
+    _check("v", v, shape)
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    B, H, N, d = shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out must be a contiguous float32 tensor shaped like q on q's device")
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    with torch.cuda.device(q.device):
+        mifa_fwd(q, k, v, out, lse, B, H, N, d, causal, scale, torch.cuda.current_stream(q.device).cuda_stream)
+    return out, lse

@@ -1,0 +1,100 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every symbol the header
+declares, and rejects every invalid argument before any HIP call (so no device is needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mifa.h")
+LIB = os.path.join(ROOT, "io_aware_softmax_mifa_amd", "libmifa.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libmifa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mifa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_expected_api():
+    assert declared_functions() == ["mifa_fwd", "mifa_last_hip_error", "mifa_status_string", "mifa_version"]
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from io_aware_softmax_mifa_amd import binding
+
+    return binding
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mifa_version().startswith("mifa ")
+    assert "gfx950" in lib.mifa_version()
+    for code in range(8):
+        s = lib.mifa_status_string(code)
+        assert s and s != "unknown status"
+    assert lib.mifa_status_string(99) == "unknown status"
+    assert lib.mifa_status_string(-1) == "unknown status"
+    assert lib.mifa_last_hip_error() == 0
+
+
+A = 1 << 20  # a fake, 16-byte aligned "device" address; never dereferenced on these paths
+
+
+@pytest.mark.parametrize(
+    "args,status",
+    [
+        ((0, A, A, A, A, 1, 1, 128, 64, 0, 0.125), 1),
+        ((A, 0, A, A, A, 1, 1, 128, 64, 0, 0.125), 1),
+        ((A, A, 0, A, A, 1, 1, 128, 64, 0, 0.125), 1),
+        ((A, A, A, 0, A, 1, 1, 128, 64, 0, 0.125), 1),
+        ((A, A, A, A, 0, 1, 1, 128, 64, 0, 0.125), 1),
+        ((A, A, A, A, A, 0, 1, 128, 64, 0, 0.125), 2),
+        ((A, A, A, A, A, 1, 0, 128, 64, 0, 0.125), 2),
+        ((A, A, A, A, A, 1, 1, 0, 64, 0, 0.125), 2),
+        ((A, A, A, A, A, -3, 1, 128, 64, 0, 0.125), 2),
+        ((A, A, A, A, A, 1, 1, 128, 32, 0, 0.125), 3),
+        ((A, A, A, A, A, 1, 1, 128, 96, 1, 0.125), 3),
+        ((A, A, A, A, A, 1, 1, 128, 256, 0, 0.125), 3),
+        ((A + 2, A, A, A, A, 1, 1, 128, 64, 0, 0.125), 4),
+        ((A, A + 8, A, A, A, 1, 1, 128, 64, 0, 0.125), 4),
+        ((A, A, A + 4, A, A, 1, 1, 128, 64, 0, 0.125), 4),
+        ((A, A, A, A + 12, A, 1, 1, 128, 64, 0, 0.125), 4),
+        ((A, A, A, A, A + 2, 1, 1, 128, 64, 0, 0.125), 4),
+        ((A, A, A, A, A, 1, 1, 128, 64, 0, float("nan")), 5),
+        ((A, A, A, A, A, 1, 1, 128, 64, 1, float("inf")), 5),
+        ((A, A, A, A, A, 1, 1, 128, 64, 0, float("-inf")), 5),
+        ((A, A, A, A, A, 1, 1, 1 << 24, 128, 0, 0.1), 6),
+        ((A, A, A, A, A, 1 << 20, 1 << 12, 1 << 10, 64, 0, 0.1), 6),
+    ],
+)
+def test_validation_rejects_before_any_hip_call(lib, args, status):
+    got = lib.mifa_fwd_raw(*args, None)
+    assert got == status, (args, got, lib.mifa_status_string(got))
+
+
+def test_validation_order_null_before_shape(lib):
+    # Several problems at once: the first failing check in the documented order wins.
+    assert lib.mifa_fwd_raw(0, A, A, A, A, 0, 0, 0, 7, 0, float("nan"), None) == 1
+    assert lib.mifa_fwd_raw(A, A, A, A, A, 0, 1, 1, 7, 0, float("nan"), None) == 2
+    assert lib.mifa_fwd_raw(A, A, A, A, A, 1, 1, 1, 7, 0, float("nan"), None) == 3
+    assert lib.mifa_fwd_raw(A + 1, A, A, A, A, 1, 1, 1, 64, 0, float("nan"), None) == 4
+
+
+def test_binding_python_checks(lib):
+    import torch
+
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        lib.attention(q, q, q)  # CPU tensors are rejected before any call

@@ -1,0 +1,217 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused attention forward (libmifa) on one MI355X.
+
+One step = one mifa_fwd launch over one batch of the workload (default: B=1, H=32, N=16384,
+d=128, causal, bf16 Q/K/V ~ N(0,1), the long-context configuration the throughput target is
+quoted on).  Inputs are generated with a seeded CPU generator and are resident in HBM before
+the timed region.  Prints ONE JSON line on stdout.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C4] [--no-cpu-baseline]
+
+FLOPs per step follow the usual attention convention: 4*B*H*N^2*d, halved for causal.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+KERNEL_SOURCE = os.path.join(ROOT, "io_aware_softmax_mifa_amd", "csrc", "mifa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def flops(w) -> float:
+    f = 4.0 * w.B * w.H * w.N * w.N * w.d
+    return f / 2 if w.causal else f
+
+
+def compulsory_bytes(w) -> int:
+    """bf16 Q, K, V read once; fp32 O and LSE written once."""
+    n = w.B * w.H * w.N
+    return 3 * 2 * n * w.d + 4 * n * w.d + 4 * n
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+    counters were taken on another kernel source or another workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get("workloads", {}).get(workload)
+    if not entry or t.get("kernel_source_sha256") != kernel_sha():
+        return None
+    return entry.get("traffic_bytes")
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return 1
+
+
+def cpu_baseline(w, q, k, v, scale, rows_count: int):
+    """The float64 oracle as it stands, timed on this host on a bounded sample of rows."""
+    from io_aware_softmax_mifa_amd import workloads as W
+    from oracle import attention_fp64_rows
+
+    rows = W.sample_rows(w.B, w.H, w.N, rows_count, w.seed + 7)
+    t0 = time.perf_counter()
+    attention_fp64_rows(q, k, v, rows, causal=w.causal, scale=scale)
+    dt = time.perf_counter() - t0
+    # Credit each sampled row with the per-row share of the step's FLOP convention.
+    per_row = flops(w) / (w.B * w.H * w.N)
+    value = rows.shape[0] * per_row / dt / 1e12
+    return {
+        "value": value,
+        "unit": "TFLOP/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": (f"{rows.shape[0]} seeded query rows of the same workload (float64 NumPy oracle, full "
+                   f"score row per query), {dt:.2f} s; credited {per_row:.3e} FLOP per row"),
+        "seconds": dt,
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="C4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the kernel has no "
+              "multi-GPU path: heads shard across GPUs with no communication, so the per-GPU figure is the "
+              "one-GPU run on that GPU's share).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from io_aware_softmax_mifa_amd import binding
+    from io_aware_softmax_mifa_amd import workloads as W
+
+    w = W.by_name(args.workload)
+    scale = W.fp32_scale(w.d)
+    log(f"workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} dist={w.dist}")
+    q, k, v = W.make_workload_inputs(w)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dq, dk, dv = (t.to(dev) for t in (q, k, v))
+    o = torch.empty(w.shape, dtype=torch.float32, device=dev)
+    lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        binding.mifa_fwd(dq, dk, dv, o, lse, w.B, w.H, w.N, w.d, w.causal, scale, stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {kernel_ms:.4f} ms/launch (HIP events)")
+
+    f = flops(w)
+    value = f / (ms_per_step * 1e-3) / 1e12
+    achieved = f / (kernel_ms * 1e-3) / 1e12
+    cb = compulsory_bytes(w)
+
+    if args.copy_calibration:
+        # A plain device-to-device copy of 1 GiB: its FETCH_SIZE / WRITE_SIZE counters give the
+        # scale from counter units to bytes.
+        n = 1 << 29
+        a = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {2 * n} bytes")
+        del a, b
+
+    out = {
+        "metric": "attention fwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. bf16 Q/K/V)",
+        "config": {
+            "workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={int(w.causal)} "
+                        f"bf16 Q,K,V ~ {'N(0,1)' if w.dist == 'normal' else 'stress'}; fp32 O + LSE",
+            "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": bool(w.causal),
+            "flop_per_step": f,
+            "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+            "kernel_ms": kernel_ms,
+            "compulsory_hbm_bytes": cb,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": measured_traffic(w.name),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_rows} sampled rows")
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, scale, args.cpu_rows)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -29,7 +29,7 @@ def flags(extra=()):
     return [
         f"--offload-arch={ARCH}",
         "-O3",
-        "-std=c++17",
+        "-std=c++20",
         "-fPIC",
         "-shared",
         f"-I{INCLUDE}",

@@ -14,14 +14,20 @@
 //  * Each wave owns 32 query rows.  Its Q rows stay in VGPRs for the whole kernel, already in
 //    the B-operand layout of v_mfma_f32_32x32x16_bf16.
 //  * K and V blocks of BC keys are streamed from HBM/L2 into double-buffered LDS with the
-//    16-byte global->LDS DMA (global_load_lds_dwordx4), so loads of block j+1 overlap the math
-//    of block j without passing through VGPRs.  A wait on the vector-memory counter plus a
-//    workgroup barrier guards each buffer before use: the threads fill the tile cooperatively,
-//    so nobody may read it before everyone's part has landed (the point made about shared
-//    SRAM in "Show HN: Flash Attention in ~100 lines of CUDA").
+//    16-byte global->LDS DMA (global_load_lds_dwordx4), without passing through VGPRs.  The
+//    threads fill a tile cooperatively, so nobody may read it before everyone's part has
+//    landed (the point made about shared SRAM in "Show HN: Flash Attention in ~100 lines of
+//    CUDA"): each block starts with a wait on the vector-memory counter and one workgroup
+//    barrier, and the next DMA is issued only after that barrier, when every wave is done
+//    with the buffer it overwrites.
 //  * Scores are computed transposed, S^T = K Q^T, on MFMA.  In the 32x32 accumulator layout a
 //    lane then holds 16 scores of ONE query (its lane % 32), so the row max and row sum are
-//    in-lane reductions plus a single exchange with lane ^ 32.
+//    in-lane reductions plus one v_permlane32_swap with the other half of the wave.
+//  * Each wave is software-pipelined over key blocks: while its VALU runs the softmax of block
+//    j, its MFMAs compute the scores of block j+1 (K runs one block ahead of V in LDS), and
+//    then the PV product of block j follows.  K and V^T operands are read from LDS through
+//    small register rings with explicit waits, so the MFMA chains never stall on a read that
+//    could have been issued earlier.
 //  * Softmax runs in the log2 domain (exp2 on v_exp_f32, with scale * log2(e) folded into one
 //    FMA per score).  The running max used for exponentiation is only raised when a block's
 //    max exceeds it by more than kRescaleSlack (2^8): the output and row sum are then
@@ -33,6 +39,8 @@
 //    contraction index), and V^T comes from LDS with ds_read_b64_tr_b16, which transposes a
 //    4 x 16 block of bf16 across each 16-lane group.  Each lane accumulates O for its own
 //    query, so the per-row rescale and the final 1/l are in-lane multiplies.
+//  * Only the blocks that straddle the causal diagonal or the end of the sequence run the
+//    masking code; all other blocks take a mask-free path.
 //  * LDS tiles are XOR-swizzled in 16-byte chunks to spread the K reads and the V transpose
 //    reads over the banks.
 //  * Grid: one workgroup per (b, h, q-tile), heaviest causal tiles first, and when the tile
@@ -40,6 +48,8 @@
 //    to the 8 XCDs round-robin) so K/V re-reads hit that XCD's L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <utility>
 
 #include "mifa.h"
 
@@ -54,6 +64,9 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) const void global_cvoid;
+
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
@@ -74,68 +87,340 @@ __device__ __forceinline__ int swz_v(int r) {
   return D == 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1);
 }
 
-__device__ __forceinline__ void wait_vmcnt(int n) {
-  // s_waitcnt with expcnt and lgkmcnt at their maxima: only the vector-memory count is waited on.
-  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14].
-  switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-  }
+__device__ __forceinline__ void wait_vmcnt0() {
+  // s_waitcnt vmcnt(0) with expcnt and lgkmcnt at their maxima (gfx9 encoding:
+  // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 }
 
-template <int D, int BC, bool CAUSAL>
+// ---- LDS operand reads ------------------------------------------------------------------------
+// Issued as inline asm so that the compiler does not treat them as reads of the LDS buffer the
+// next DMA is filling (which would make it drain that DMA first).  Every consumer waits through
+// lgkm_wait, which ties the registers that must have landed to the s_waitcnt; LDS reads complete
+// in issue order, so "at most N outstanding" means everything but the N most recent is done.
+template <int OFF>
+__device__ __forceinline__ bf16x8 lds_read_b128(unsigned addr) {
+  bf16x8 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ i16x4 lds_read_tr(unsigned addr) {
+  i16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
+  return r;
+}
+template <int N, typename R>
+__device__ __forceinline__ void lgkm_wait(R& r) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "i"(N));
+}
+template <int N, typename R>
+__device__ __forceinline__ void lgkm_wait(R& a, R& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
+
+// ---- small VALU helpers ------------------------------------------------------------------------
+// Maximum without the NaN-quieting canonicalisation that fmaxf needs (scores are never NaN);
+// three-operand forms map onto v_maximum3_f32.
+__device__ __forceinline__ float fmax2(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float fmax3(float a, float b, float c) { return fmax2(fmax2(a, b), c); }
+
+// v_permlane32_swap exchanges the two 32-lane halves of a wave.  Every lane then holds its own
+// value and the value of the lane 32 away.  (The pair is read back through a 64-bit bit cast:
+// subscripting the returned vector loses its second element with this compiler.)
+__device__ __forceinline__ void swap_halves(float x, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, x), __builtin_bit_cast(unsigned, x),
+                                                  false, false);
+  const uint64_t both = __builtin_bit_cast(uint64_t, r);
+  a = __builtin_bit_cast(float, (unsigned)both);
+  b = __builtin_bit_cast(float, (unsigned)(both >> 32));
+}
+__device__ __forceinline__ float half_max(float x) {
+  float a, b;
+  swap_halves(x, a, b);
+  return fmax2(a, b);
+}
+__device__ __forceinline__ float half_sum(float x) {
+  float a, b;
+  swap_halves(x, a, b);
+  return a + b;
+}
+
+// ---- tile geometry -----------------------------------------------------------------------------
+template <int D, int BC>
 struct Tile {
-  static constexpr int kChunksPerRow = D / 8;             // 16-byte chunks per K/V row
-  static constexpr int kRowsPerInst = 64 / kChunksPerRow; // rows one wave-wide DMA covers
+  static constexpr int kChunksPerRow = D / 8;              // 16-byte chunks per K/V row
+  static constexpr int kRowsPerInst = 64 / kChunksPerRow;  // rows one wave-wide DMA covers
   static constexpr int kInstPerTensor = BC / kRowsPerInst;
   static constexpr int kInstPerWave = kInstPerTensor / kWaves;
-  static constexpr int kLoadsPerBlock = 2 * kInstPerWave; // K and V DMA ops per thread per block
   static constexpr int kTensorBytes = BC * D * 2;
-  static constexpr int kBufBytes = 2 * kTensorBytes;      // K then V
-  static constexpr int kLdsBytes = 2 * kBufBytes;         // double buffered
+  // LDS: K buffers 0 and 1, then V buffers 0 and 1.
+  static constexpr int kKOff0 = 0, kKOff1 = kTensorBytes;
+  static constexpr int kVOff0 = 2 * kTensorBytes, kVOff1 = 3 * kTensorBytes;
+  static constexpr int kLdsBytes = 4 * kTensorBytes;
+  static constexpr int kDS = D / 16;  // 16-wide d slices of the S^T MFMA
+  static constexpr int kDT = D / 32;  // 32-row dv tiles of O^T
+  static constexpr int kKT = BC / 32; // 32-key tiles per block
+  static constexpr int kKS = BC / 16; // 16-key slices per block (PV k-steps)
+  static constexpr int kSSteps = kKT * kDS;  // MFMAs per S^T block
+  static constexpr int kPVSteps = kKS * kDT; // MFMAs per PV block
   static_assert(kInstPerTensor % kWaves == 0, "block must split evenly over the waves");
   static_assert(BC % 32 == 0, "key block must be a multiple of the 32-key MFMA tile");
+  static_assert(kLdsBytes <= 65536, "immediate LDS offsets must fit in 16 bits");
 };
 
-// Issue the DMA of key block `blk` (rows blk*BC ..) of K and V into LDS buffer `buf`.
-// Rows past N are clamped to N-1: they are masked out of the softmax, and clamping keeps every
-// global address inside the tensors.
-template <int D, int BC, bool CAUSAL>
-__device__ __forceinline__ void issue_kv(const __bf16* __restrict__ kbase, const __bf16* __restrict__ vbase,
-                                        char* smem_buf, int blk, int N, int wave, int lane) {
-  using T = Tile<D, BC, CAUSAL>;
+// ---- per-lane addressing, fixed for the whole kernel -----------------------------------------
+template <int D, int BC>
+struct Lane {
+  unsigned k;            // K operand of slice 0, tile 0, buffer 0; slice s XORs 32*s
+  unsigned v[D / 32];    // V^T operand of dv tile t, key slice 0, buffer 0
+  unsigned dk[Tile<D, BC>::kInstPerWave];  // DMA source byte offsets within a key block (K)
+  unsigned dv[Tile<D, BC>::kInstPerWave];  // (V)
+};
+
+// DMA: instruction t of this wave covers rows inst*kRowsPerInst .. of the block; lane ->
+// (row, physical chunk); the source is the logical chunk that the swizzle places there.  Rows
+// past `row_limit` are clamped to it (only the last, partial block needs that).
+template <int D, int BC>
+__device__ __forceinline__ void dma_offsets(unsigned* dk, unsigned* dv, int wave, int lane, int row_limit) {
+  using T = Tile<D, BC>;
 #pragma unroll
   for (int t = 0; t < T::kInstPerWave; ++t) {
     const int inst = wave * T::kInstPerWave + t;
     const int r = inst * T::kRowsPerInst + lane / T::kChunksPerRow;
     const int pc = lane % T::kChunksPerRow;
-    int grow = blk * BC + r;
-    grow = grow < N ? grow : N - 1;
-    const __bf16* ks = kbase + (int64_t)grow * D + ((pc ^ swz_k<D>(r)) * 8);
-    const __bf16* vs = vbase + (int64_t)grow * D + ((pc ^ swz_v<D>(r)) * 8);
-    __builtin_amdgcn_global_load_lds((global_cvoid*)ks, (lds_void*)(smem_buf + inst * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((global_cvoid*)vs,
-                                     (lds_void*)(smem_buf + T::kTensorBytes + inst * 1024), 16, 0, 0);
+    const int rr = r < row_limit ? r : row_limit;
+    dk[t] = (unsigned)(rr * (D * 2) + ((pc ^ swz_k<D>(r)) * 16));
+    dv[t] = (unsigned)(rr * (D * 2) + ((pc ^ swz_v<D>(r)) * 16));
   }
 }
 
-__device__ __forceinline__ float xor32(float x) {
-  return __shfl_xor(x, 32, 64);
+template <int D, int BC>
+__device__ __forceinline__ Lane<D, BC> lane_setup(unsigned smem_base, int wave, int lane) {
+  using T = Tile<D, BC>;
+  Lane<D, BC> a;
+  const int ln = lane & 31, hf = lane >> 5;
+  a.k = smem_base + ln * (D * 2) + ((hf ^ swz_k<D>(ln)) * 16);
+  const int g = lane >> 4, p = lane & 15;
+  const int dvh = g & 1;
+  const int r = 4 * hf + (p >> 2);          // row within a 16-key slice, half e = 0
+  const int cl = 2 * dvh + ((p & 3) >> 1);  // chunk within a 32-wide dv tile
+  const unsigned base = smem_base + r * (D * 2) + (p & 1) * 8;
+#pragma unroll
+  for (int t = 0; t < T::kDT; ++t) a.v[t] = base + (((4 * t + cl) ^ swz_v<D>(r)) * 16);
+  dma_offsets<D, BC>(a.dk, a.dv, wave, lane, BC);
+  return a;
 }
+
+// Issue the DMA of key block `blk` of K (if do_k) and V (if do_v) into buffer `buf`.  The block
+// base is wave-uniform, the per-lane part a 32-bit byte offset.
+template <int D, int BC>
+__device__ __forceinline__ void issue_dma(const __bf16* __restrict__ kbase, const __bf16* __restrict__ vbase,
+                                          char* smem, int buf, int blk, int N, int wave, int lane,
+                                          const Lane<D, BC>& la, bool do_k, bool do_v) {
+  using T = Tile<D, BC>;
+  const char* kb = (const char*)(kbase + (int64_t)blk * BC * D);
+  const char* vb = (const char*)(vbase + (int64_t)blk * BC * D);
+  unsigned dk[T::kInstPerWave], dv[T::kInstPerWave];
+#pragma unroll
+  for (int t = 0; t < T::kInstPerWave; ++t) {
+    dk[t] = la.dk[t];
+    dv[t] = la.dv[t];
+  }
+  // In the last, partial block, rows past N are clamped to N-1: they are masked out of the
+  // softmax, and clamping keeps every global address inside the tensors.
+  if (blk * BC + BC > N) dma_offsets<D, BC>(dk, dv, wave, lane, N - 1 - blk * BC);
+  char* kdst = smem + (buf ? T::kKOff1 : T::kKOff0);
+  char* vdst = smem + (buf ? T::kVOff1 : T::kVOff0);
+#pragma unroll
+  for (int t = 0; t < T::kInstPerWave; ++t) {
+    const int inst = wave * T::kInstPerWave + t;
+    if (do_k)
+      __builtin_amdgcn_global_load_lds((global_cvoid*)(kb + dk[t]), (lds_void*)(kdst + inst * 1024), 16, 0, 0);
+    if (do_v)
+      __builtin_amdgcn_global_load_lds((global_cvoid*)(vb + dv[t]), (lds_void*)(vdst + inst * 1024), 16, 0, 0);
+  }
+}
+
+// ---- the per-wave pipeline stages -------------------------------------------------------------
+template <int D, int BC, bool CAUSAL>
+struct Wave {
+  using T = Tile<D, BC>;
+  static constexpr int kKR = 3;    // K operand ring depth (S^T reads run kKR-1 MFMAs ahead)
+  static constexpr int kVLook = 2; // V^T reads run kVLook PV steps ahead
+  static constexpr int kVR = 2 * (kVLook + 1);
+
+  bf16x8 qf[T::kDS];
+  f32x16 oacc[T::kDT];
+  float m_run;  // running max in log2 units (stale by at most kRescaleSlack)
+  float l_run;  // this lane's half of the row sum
+  float c;      // |scale| * log2(e), >= 1e-30
+  int N, row0, my_row, hf;
+  Lane<D, BC> la;
+
+  // ---- S^T = K Q^T for one block: step i is d slice i / kKT of key tile i % kKT ----
+  template <int KB, int I>
+  __device__ __forceinline__ void issue_k(bf16x8 (&kr)[kKR], IC<I>) {
+    constexpr int s = I / T::kKT, kt = I % T::kKT;
+    constexpr int off = (KB ? T::kKOff1 : T::kKOff0) + kt * 32 * D * 2;
+    kr[I % kKR] = lds_read_b128<off>(la.k ^ (32u * s));
+  }
+  template <int KB>
+  __device__ __forceinline__ void s_start(bf16x8 (&kr)[kKR]) {
+    [&]<int... I>(std::integer_sequence<int, I...>) { (issue_k<KB>(kr, IC<I>{}), ...); }(
+        std::make_integer_sequence<int, kKR>{});
+  }
+  template <int KB, int I>
+  __device__ __forceinline__ void s_step(f32x16 (&sacc)[T::kKT], bf16x8 (&kr)[kKR], IC<I>) {
+    constexpr int n = T::kSSteps;
+    constexpr int after = (I + kKR < n ? I + kKR : n) - I - 1;  // K reads issued after read I
+    lgkm_wait<after>(kr[I % kKR]);
+    const bf16x8 a = kr[I % kKR];
+    if constexpr (I + kKR < n) issue_k<KB>(kr, IC<I + kKR>{});
+    constexpr int s = I / T::kKT, kt = I % T::kKT;
+    if constexpr (s == 0)
+      sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], (f32x16){}, 0, 0, 0);
+    else
+      sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
+  }
+  template <int KB, int LO, int HI>
+  __device__ __forceinline__ void s_steps(f32x16 (&sacc)[T::kKT], bf16x8 (&kr)[kKR]) {
+    [&]<int... I>(std::integer_sequence<int, I...>) { (s_step<KB>(sacc, kr, IC<LO + I>{}), ...); }(
+        std::make_integer_sequence<int, HI - LO>{});
+  }
+
+  // ---- softmax, part 1: mask (diagonal / tail blocks), block row max, rescale decision ----
+  __device__ __forceinline__ void apply_mask(f32x16 (&sacc)[T::kKT], int key0) {
+    // Key offset 32kt + 8(i/4) + (i%4) within the block is visible iff it is <= lim.
+    int lim = N - 1 - key0 - 4 * hf;
+    if (CAUSAL) lim = min(lim, my_row - key0 - 4 * hf);
+#pragma unroll
+    for (int kt = 0; kt < T::kKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int off = 32 * kt + 8 * (i >> 2) + (i & 3);
+        sacc[kt][i] = off <= lim ? sacc[kt][i] : -__builtin_inff();
+      }
+  }
+  __device__ __forceinline__ bool softmax_max(const f32x16 (&sacc)[T::kKT], float& bm) {
+    float mx4[2 * T::kKT];
+#pragma unroll
+    for (int kt = 0; kt < T::kKT; ++kt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = 8 * h;
+        float m = fmax3(sacc[kt][i], sacc[kt][i + 1], sacc[kt][i + 2]);
+        m = fmax3(m, sacc[kt][i + 3], sacc[kt][i + 4]);
+        m = fmax3(m, sacc[kt][i + 5], sacc[kt][i + 6]);
+        mx4[2 * kt + h] = fmax2(m, sacc[kt][i + 7]);
+      }
+    static_assert(T::kKT == 2, "row max written for two 32-key tiles");
+    const float mx = half_max(fmax2(fmax3(mx4[0], mx4[1], mx4[2]), mx4[3]));
+    bm = mx * c;  // block max in log2 units; c > 0 keeps an all-masked row at -inf
+    return bm > m_run + kRescaleSlack;
+  }
+
+  __device__ __forceinline__ void rescale(bool grow, float bm) {
+    const float m_new = grow ? bm : m_run;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+    l_run *= alpha;
+#pragma unroll
+    for (int t = 0; t < T::kDT; ++t) oacc[t] *= alpha;
+    m_run = m_new;
+  }
+
+  // ---- softmax, part 2: P = exp2(S * c - m) packed to bf16, and the row sum ----
+  // A masked score is -inf and c > 0, so its weight is exp2(-inf) = 0.
+  __device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[T::kKT], bf16x8 (&pb)[T::kKS]) {
+    float ls4[4];
+    const float neg_m = -m_run;
+#pragma unroll
+    for (int kt = 0; kt < T::kKT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][i], c, neg_m));
+        if (kt == 0 && i < 4)
+          ls4[i] = p;
+        else
+          ls4[i & 3] += p;
+        pb[2 * kt + (i >> 3)][i & 7] = (__bf16)p;
+      }
+    l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+  }
+
+  // ---- O^T += V^T P^T for one block from V buffer VB ----
+  // Step st multiplies key slice st / kDT into dv tile st % kDT.  Lane (dv row 32t + ln, half hf)
+  // needs V[key][dv] for keys 16ks + 4hf + 0..3 (read "lo") and 16ks + 8 + 4hf + 0..3 (read
+  // "hi"); the transpose read hands each lane of a 16-lane group its dv column of a 4-key slab.
+  template <int VB, int ST>
+  __device__ __forceinline__ void issue_v(i16x4 (&vr)[kVR], IC<ST>) {
+    constexpr int ks = ST / T::kDT, t = ST % T::kDT;
+    constexpr int slot = ST % (kVLook + 1);
+    constexpr int off = (VB ? T::kVOff1 : T::kVOff0) + ks * 16 * D * 2;
+    vr[2 * slot] = lds_read_tr<off>(la.v[t]);
+    vr[2 * slot + 1] = lds_read_tr<off + 8 * D * 2>(la.v[t]);
+  }
+  template <int VB>
+  __device__ __forceinline__ void pv_start(i16x4 (&vr)[kVR]) {
+    [&]<int... I>(std::integer_sequence<int, I...>) { (issue_v<VB>(vr, IC<I>{}), ...); }(
+        std::make_integer_sequence<int, kVLook>{});
+  }
+  template <int VB, int ST>
+  __device__ __forceinline__ void pv_step(const bf16x8 (&pb)[T::kKS], i16x4 (&vr)[kVR], IC<ST>) {
+    constexpr int n = T::kPVSteps;
+    constexpr int ks = ST / T::kDT, t = ST % T::kDT;
+    constexpr int slot = ST % (kVLook + 1);
+    constexpr int ahead = (ST + kVLook < n ? ST + kVLook : n) - ST - 1;  // steps issued after this one
+    lgkm_wait<2 * ahead>(vr[2 * slot], vr[2 * slot + 1]);
+    const i16x8 a16 = __builtin_shufflevector(vr[2 * slot], vr[2 * slot + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+    if constexpr (ST + kVLook < n) issue_v<VB>(vr, IC<ST + kVLook>{});
+    // (On the causal diagonal, slices above this wave's rows have all-zero weights; they are
+    // multiplied anyway, which keeps this path free of branches.)
+    oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16), pb[ks], oacc[t], 0, 0, 0);
+  }
+  template <int VB>
+  __device__ __forceinline__ void pv(const bf16x8 (&pb)[T::kKS], i16x4 (&vr)[kVR]) {
+    [&]<int... St>(std::integer_sequence<int, St...>) { (pv_step<VB>(pb, vr, IC<St>{}), ...); }(
+        std::make_integer_sequence<int, T::kPVSteps>{});
+  }
+
+  // ---- one key block j, with the scores of block j+1 computed alongside ----
+  // `cur` holds S^T(j) on entry and `nxt` holds S^T(j+1) on exit.  K(j+1) is in K buffer
+  // KB = (j+1) & 1 and V(j) in V buffer VB = j & 1.  The first half of the S^T(j+1) MFMAs sits
+  // with the row max, the second half with the exponentials, so MFMA and VALU work interleave.
+  // On the last block K buffer KB holds no block and the scores computed from it are unused.
+  template <int KB, int VB>
+  __device__ __forceinline__ void block(f32x16 (&cur)[T::kKT], f32x16 (&nxt)[T::kKT], int key0, bool masked) {
+    bf16x8 kr[kKR];
+    constexpr int half = T::kSSteps / 2;
+    if (masked) apply_mask(cur, key0);
+    s_start<KB>(kr);
+    s_steps<KB, 0, half>(nxt, kr);
+    float bm;
+    const bool grow = softmax_max(cur, bm);
+    if (__builtin_amdgcn_ballot_w64(grow)) rescale(grow, bm);
+    bf16x8 pb[T::kKS];
+    s_steps<KB, half, T::kSSteps>(nxt, kr);
+    softmax_exp(cur, pb);
+    i16x4 vr[kVR];
+    pv_start<VB>(vr);
+    pv<VB>(pb, vr);
+  }
+
+  // Scores of the first block (no softmax to overlap with).
+  __device__ __forceinline__ void first_scores(f32x16 (&s)[T::kKT]) {
+    bf16x8 kr[kKR];
+    s_start<0>(kr);
+    s_steps<0, 0, T::kSSteps>(s, kr);
+  }
+};
 
 template <int D, int BC, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, float* __restrict__ o, float* __restrict__ lse,
                      int N, int BH, int n_qtiles, float c_log2, int negate_q, int xcd_group) {
-  using T = Tile<D, BC, CAUSAL>;
-  constexpr int kDS = D / 16;  // 16-wide d slices of the S^T MFMA
-  constexpr int kDT = D / 32;  // 32-row dv tiles of O^T
-  constexpr int kKT = BC / 32; // 32-key tiles per block
-  constexpr int kKS = BC / 16; // 16-key slices per block (PV k-steps)
-
+  using T = Tile<D, BC>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int tid = threadIdx.x;
@@ -167,182 +452,105 @@ void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const __bf16* __restrict__ kh = k + head_off;
   const __bf16* __restrict__ vh = v + head_off;
 
-  const int row0 = qt * kBR + wave * kRowsPerWave;  // first query row of this wave
-  const int my_row = row0 + ln;
+  Wave<D, BC, CAUSAL> W;
+  W.N = N;
+  W.row0 = qt * kBR + wave * kRowsPerWave;
+  W.my_row = W.row0 + ln;
+  W.hf = hf;
+  W.c = c_log2;
+  W.m_run = -__builtin_inff();
+  W.l_run = 0.f;
+#pragma unroll
+  for (int t = 0; t < T::kDT; ++t) W.oacc[t] = (f32x16){};
 
   // ---- Q rows into VGPRs (B operand of S^T = K Q^T: lane holds q[row][16s + 8hf .. +7]) ----
-  bf16x8 qf[kDS];
   {
-    const int r = my_row < N ? my_row : N - 1;
+    const int r = W.my_row < N ? W.my_row : N - 1;
     const __bf16* src = qh + (int64_t)r * D + 8 * hf;
 #pragma unroll
-    for (int s = 0; s < kDS; ++s) {
+    for (int s = 0; s < T::kDS; ++s) {
       u32x4 raw = *(const u32x4*)(src + 16 * s);
       if (negate_q) raw ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-      qf[s] = __builtin_bit_cast(bf16x8, raw);
+      W.qf[s] = __builtin_bit_cast(bf16x8, raw);
     }
   }
 
+  // Blocks [0, nblk) are visited; blocks [j_mask, nblk) straddle the diagonal or the end of the
+  // sequence and take the masked path.
   const int n_kblocks = (N + BC - 1) / BC;
   int nblk = n_kblocks;
+  int j_mask = N / BC;
   if (CAUSAL) {
     const int last_row = min(N - 1, qt * kBR + kBR - 1);
     nblk = last_row / BC + 1;
+    j_mask = min(j_mask, (qt * kBR) / BC);
   }
 
-  f32x16 oacc[kDT];
-#pragma unroll
-  for (int t = 0; t < kDT; ++t) oacc[t] = (f32x16){};
-  float m_run = -__builtin_inff();  // running max in log2 units (stale by at most kRescaleSlack)
-  float l_run = 0.f;                // this lane's half of the row sum
+  const unsigned smem_base = (unsigned)(uintptr_t)(lds_void*)smem;
+  W.la = lane_setup<D, BC>(smem_base, wave, lane);
 
-  issue_kv<D, BC, CAUSAL>(kh, vh, smem, 0, N, wave, lane);
+  // ---- prologue: K(0), V(0) and K(1) in flight; scores of block 0 ----
+  issue_dma<D, BC>(kh, vh, smem, 0, 0, N, wave, lane, W.la, true, true);
+  if (nblk > 1) issue_dma<D, BC>(kh, vh, smem, 1, 1, N, wave, lane, W.la, true, false);
+  wait_vmcnt0();
+  __builtin_amdgcn_s_barrier();
 
-  for (int j = 0; j < nblk; ++j) {
-    char* buf = smem + (j & 1) * T::kBufBytes;
-    if (j + 1 < nblk) {
-      issue_kv<D, BC, CAUSAL>(kh, vh, smem + ((j + 1) & 1) * T::kBufBytes, j + 1, N, wave, lane);
-      wait_vmcnt(T::kLoadsPerBlock);
-    } else {
-      wait_vmcnt(0);
-    }
+  f32x16 sA[T::kKT], sB[T::kKT];
+  W.first_scores(sA);
+
+  // ---- main loop, unrolled by two so buffer parities are compile-time ----
+  // At block j: wait for K(j+1) and V(j), barrier (every wave is done with block j-1, whose
+  // buffers are the ones refilled next), issue K(j+2) and V(j+1), then the block itself.
+  auto step = [&](auto par_c, int j, f32x16(&cur)[T::kKT], f32x16(&nxt)[T::kKT]) {
+    constexpr int P = decltype(par_c)::value;  // j & 1
+    wait_vmcnt0();
     __builtin_amdgcn_s_barrier();
-
-    const int key0 = j * BC;
-    // Wave-uniform facts about this block.
-    const bool wave_dead = CAUSAL && key0 > row0 + kRowsPerWave - 1;  // all keys above the diagonal
-    const bool need_mask = (CAUSAL && key0 + BC - 1 > row0) || (key0 + BC > N);
-
-    if (!wave_dead) {
-      const char* sk = buf;
-      const char* sv = buf + T::kTensorBytes;
-
-      // ---- S^T = K_j Q^T on MFMA ----
-      f32x16 sacc[kKT];
-#pragma unroll
-      for (int kt = 0; kt < kKT; ++kt) {
-        sacc[kt] = (f32x16){};
-        const bool tile_live = !CAUSAL || key0 + 32 * kt <= row0 + kRowsPerWave - 1;
-        if (tile_live) {
-          const int r = 32 * kt + ln;
-#pragma unroll
-          for (int s = 0; s < kDS; ++s) {
-            const int c = 2 * s + hf;
-            const bf16x8 a = *(const bf16x8*)(sk + r * (D * 2) + ((c ^ swz_k<D>(r)) * 16));
-            sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
-          }
-        }
-      }
-
-      // ---- mask, block row max ----
-      // Lane holds S^T[key][my_row] for key = key0 + 32kt + 8(i/4) + 4hf + (i%4).
-      float mx = -__builtin_inff();
-      if (need_mask) {
-#pragma unroll
-        for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + 32 * kt + 8 * (i >> 2) + 4 * hf + (i & 3);
-            const bool vis = key < N && (!CAUSAL || key <= my_row);
-            sacc[kt][i] = vis ? sacc[kt][i] : -__builtin_inff();
-          }
-      }
-#pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(sacc[kt][i], sacc[kt][i + 1]));
-      mx = fmaxf(mx, xor32(mx));
-      // Block max in log2 units; c_log2 >= 0, and an all-masked row stays at -inf.
-      const float bm = mx == -__builtin_inff() ? mx : mx * c_log2;
-
-      // ---- lazy rescale: only when the block max outgrows the running max by the slack ----
-      const bool grow = bm > m_run + kRescaleSlack;
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-        const float m_new = grow ? bm : m_run;
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
-        l_run *= alpha;
-#pragma unroll
-        for (int t = 0; t < kDT; ++t) oacc[t] *= alpha;
-        m_run = m_new;
-      }
-
-      // ---- P = exp2(S * c - m), row sum, bf16 pack (B operand of O^T += V^T P^T) ----
-      bf16x8 pb[kKS];
-      float lsum = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < kKT; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][i], c_log2, -m_run));
-          if (need_mask) p = sacc[kt][i] == -__builtin_inff() ? 0.f : p;
-          lsum += p;
-          pb[2 * kt + (i >> 3)][i & 7] = (__bf16)p;
-        }
-      l_run += lsum;
-
-      // ---- O^T += V_j^T P^T on MFMA; V^T operand via the LDS transpose read ----
-      // Lane (dv row 32t + ln, half hf) needs V[key][dv] for keys 16ks + 4hf + 0..3 and
-      // 16ks + 8 + 4hf + 0..3.  Within a 16-lane group, lane p addresses key row (p / 4) of the
-      // 4-row slab and dv column 4 * (p % 4) of the group's 16 columns; the transpose read then
-      // hands lane i the group's column i of those 4 rows.
-      const int g = lane >> 4, p = lane & 15;
-      const int dvh = g & 1;
-#pragma unroll
-      for (int ks = 0; ks < kKS; ++ks) {
-        const bool slice_live = !CAUSAL || key0 + 16 * ks <= row0 + kRowsPerWave - 1;
-        if (!slice_live) continue;
-#pragma unroll
-        for (int t = 0; t < kDT; ++t) {
-          const int c = 4 * t + 2 * dvh + ((p & 3) >> 1);
-          const int sub = (p & 1) * 8;
-          const int r0 = 16 * ks + 4 * hf + (p >> 2);
-          const int r1 = r0 + 8;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(lds_void*)(sv + r0 * (D * 2) + ((c ^ swz_v<D>(r0)) * 16) + sub));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(lds_void*)(sv + r1 * (D * 2) + ((c ^ swz_v<D>(r1)) * 16) + sub));
-          const i16x8 a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16), pb[ks], oacc[t], 0, 0, 0);
-        }
-      }
-    }
-    // Everyone is done with this buffer before the next iteration's DMA overwrites it.
-    __builtin_amdgcn_s_barrier();
+    if (j + 2 < nblk) issue_dma<D, BC>(kh, vh, smem, P, j + 2, N, wave, lane, W.la, true, false);
+    if (j + 1 < nblk) issue_dma<D, BC>(kh, vh, smem, P ^ 1, j + 1, N, wave, lane, W.la, false, true);
+    W.template block<P ^ 1, P>(cur, nxt, j * BC, j >= j_mask);
+  };
+  for (int j = 0; j < nblk; j += 2) {
+    step(IC<0>{}, j, sA, sB);
+    if (j + 1 >= nblk) break;
+    step(IC<1>{}, j + 1, sB, sA);
   }
 
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ----
-  const float l_tot = l_run + xor32(l_run);
-  if (my_row < N) {
+  const float l_tot = half_sum(W.l_run);
+  if (W.my_row < N) {
     const float inv = 1.f / l_tot;
-    float* orow = o + head_off + (int64_t)my_row * D;
+    float* orow = o + head_off + (int64_t)W.my_row * D;
 #pragma unroll
-    for (int t = 0; t < kDT; ++t)
+    for (int t = 0; t < T::kDT; ++t)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        f32x4 val = {oacc[t][4 * g4] * inv, oacc[t][4 * g4 + 1] * inv, oacc[t][4 * g4 + 2] * inv,
-                     oacc[t][4 * g4 + 3] * inv};
+        f32x4 val = {W.oacc[t][4 * g4] * inv, W.oacc[t][4 * g4 + 1] * inv, W.oacc[t][4 * g4 + 2] * inv,
+                     W.oacc[t][4 * g4 + 3] * inv};
         *(f32x4*)(orow + 32 * t + 8 * g4 + 4 * hf) = val;
       }
-    if (hf == 0) lse[(int64_t)bh * N + my_row] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    if (hf == 0) lse[(int64_t)bh * N + W.my_row] = (W.m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
   }
 }
 
 template <int D, int BC, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, float* o, float* lse, int N, int BH,
                   float scale, hipStream_t stream) {
-  using T = Tile<D, BC, CAUSAL>;
+  using T = Tile<D, BC>;
   const int n_qtiles = (N + kBR - 1) / kBR;
   const int64_t tiles = (int64_t)BH * n_qtiles;
   const int xcd_group = (BH % kXcds == 0) ? 1 : 0;
   const int negate_q = scale < 0.f ? 1 : 0;
-  const float c_log2 = (float)((double)(negate_q ? -scale : scale) * 1.4426950408889634);
+  // The exponent factor c = |scale| * log2(e) is kept >= 1e-30 so that a masked score (-inf)
+  // always maps to exp2(-inf) = 0.  For |scale| below that every logit is under 1e-29 in
+  // magnitude and exp2 of it rounds to exactly 1 in fp32, the same as with scale = 0.
+  double c_exact = (double)(negate_q ? -scale : scale) * 1.4426950408889634;
+  if (c_exact < 1e-30) c_exact = 1e-30;
+  const float c_log2 = (float)c_exact;
   auto kern = mifa_fwd_kernel<D, BC, CAUSAL>;
-  static bool configured = false;  // per-instantiation attribute, idempotent
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, T::kLdsBytes);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  // Raise the dynamic-LDS limit once per instantiation (thread-safe static initialisation).
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, T::kLdsBytes);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kThreads), T::kLdsBytes, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, o, lse, N, BH, n_qtiles, c_log2,
                      negate_q, xcd_group);

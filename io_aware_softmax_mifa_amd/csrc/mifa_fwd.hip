@@ -10,16 +10,19 @@
 // (FlashAttention-2 remark in the Hacker News FlashAttention-3 thread); blocks wholly above
 // the diagonal are never loaded.
 //
-// Design on gfx950 (one workgroup = 4 waves = 128 query rows of one (b, h)):
+// Design on gfx950 (one workgroup = 4 or 8 waves = 128 or 256 query rows of one (b, h)):
 //  * Each wave owns 32 query rows.  Its Q rows stay in VGPRs for the whole kernel, already in
 //    the B-operand layout of v_mfma_f32_32x32x16_bf16.
-//  * K and V blocks of BC keys are streamed from HBM/L2 into double-buffered LDS with the
+//  * K and V blocks of BC keys are streamed from HBM/L2 into 2 or 3 LDS buffers each with the
 //    16-byte global->LDS DMA (global_load_lds_dwordx4), without passing through VGPRs.  The
 //    threads fill a tile cooperatively, so nobody may read it before everyone's part has
 //    landed (the point made about shared SRAM in "Show HN: Flash Attention in ~100 lines of
 //    CUDA"): each block starts with a wait on the vector-memory counter and one workgroup
 //    barrier, and the next DMA is issued only after that barrier, when every wave is done
-//    with the buffer it overwrites.
+//    with the buffer it overwrites.  With 3 buffers a block's DMA has two block-times to land.
+//  * Large grids use 8-wave workgroups (one per CU, 96 KB of LDS): every K/V block brought into
+//    LDS then serves 256 query rows, which halves the L2->LDS stream; small grids use 4-wave
+//    workgroups (two per CU) so that enough workgroups exist to fill the 256 CUs.
 //  * Scores are computed transposed, S^T = K Q^T, on MFMA.  In the 32x32 accumulator layout a
 //    lane then holds 16 scores of ONE query (its lane % 32), so the row max and row sum are
 //    in-lane reductions plus one v_permlane32_swap with the other half of the wave.
@@ -68,10 +71,8 @@ typedef __attribute__((address_space(1))) const void global_cvoid;
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 32;
-constexpr int kBR = kWaves * kRowsPerWave;  // query rows per workgroup
-constexpr int kThreads = kWaves * 64;
+constexpr int kMaxBR = 256;                 // largest workgroup row tile (8 waves)
 constexpr float kRescaleSlack = 8.0f;       // log2 units: weights stay <= 2^8 between rescales
 constexpr int kXcds = 8;
 
@@ -84,13 +85,15 @@ __device__ __forceinline__ int swz_k(int r) {
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
-  return D == 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1);
+  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
 }
 
-__device__ __forceinline__ void wait_vmcnt0() {
-  // s_waitcnt vmcnt(0) with expcnt and lgkmcnt at their maxima (gfx9 encoding:
-  // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+// s_waitcnt vmcnt(N) with expcnt and lgkmcnt at their maxima (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // ---- LDS operand reads ------------------------------------------------------------------------
@@ -147,165 +150,174 @@ __device__ __forceinline__ float half_sum(float x) {
 }
 
 // ---- tile geometry -----------------------------------------------------------------------------
-template <int D, int BC>
-struct Tile {
+template <int D_, int BC_, int WAVES_, int NBUF_>
+struct Cfg {
+  static constexpr int D = D_, BC = BC_, WAVES = WAVES_, NBUF = NBUF_;
+  static constexpr int kBR = WAVES * kRowsPerWave;         // query rows per workgroup
+  static constexpr int kThreads = WAVES * 64;
   static constexpr int kChunksPerRow = D / 8;              // 16-byte chunks per K/V row
   static constexpr int kRowsPerInst = 64 / kChunksPerRow;  // rows one wave-wide DMA covers
   static constexpr int kInstPerTensor = BC / kRowsPerInst;
-  static constexpr int kInstPerWave = kInstPerTensor / kWaves;
+  static constexpr int kInstPerWave = kInstPerTensor / WAVES;
+  static constexpr int kDmaPerGroup = 2 * kInstPerWave;    // K + V DMA ops per thread per block
   static constexpr int kTensorBytes = BC * D * 2;
-  // LDS: K buffers 0 and 1, then V buffers 0 and 1.
-  static constexpr int kKOff0 = 0, kKOff1 = kTensorBytes;
-  static constexpr int kVOff0 = 2 * kTensorBytes, kVOff1 = 3 * kTensorBytes;
-  static constexpr int kLdsBytes = 4 * kTensorBytes;
+  // LDS: NBUF K buffers, then NBUF V buffers.
+  static constexpr int kVBase = NBUF * kTensorBytes;
+  static constexpr int kLdsBytes = 2 * NBUF * kTensorBytes;
   static constexpr int kDS = D / 16;  // 16-wide d slices of the S^T MFMA
   static constexpr int kDT = D / 32;  // 32-row dv tiles of O^T
   static constexpr int kKT = BC / 32; // 32-key tiles per block
   static constexpr int kKS = BC / 16; // 16-key slices per block (PV k-steps)
   static constexpr int kSSteps = kKT * kDS;  // MFMAs per S^T block
   static constexpr int kPVSteps = kKS * kDT; // MFMAs per PV block
-  static_assert(kInstPerTensor % kWaves == 0, "block must split evenly over the waves");
+  static_assert(kInstPerTensor % WAVES == 0 && kInstPerWave >= 1, "block must split evenly over the waves");
   static_assert(BC % 32 == 0, "key block must be a multiple of the 32-key MFMA tile");
-  static_assert(kLdsBytes <= 65536, "immediate LDS offsets must fit in 16 bits");
+  static_assert(NBUF == 2 || NBUF == 3, "double or triple buffering");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
+  static_assert((NBUF - 1) * kTensorBytes + 32 * D * 2 <= 65535, "K read immediates fit in 16 bits");
+  static_assert(BC * D * 2 <= 65535, "V read immediates fit in 16 bits");
 };
 
 // ---- per-lane addressing, fixed for the whole kernel -----------------------------------------
-template <int D, int BC>
+template <typename C>
 struct Lane {
-  unsigned k;            // K operand of slice 0, tile 0, buffer 0; slice s XORs 32*s
-  unsigned v[D / 32];    // V^T operand of dv tile t, key slice 0, buffer 0
-  unsigned dk[Tile<D, BC>::kInstPerWave];  // DMA source byte offsets within a key block (K)
-  unsigned dv[Tile<D, BC>::kInstPerWave];  // (V)
+  unsigned k;                   // K operand of slice 0, tile 0, K buffer 0; slice s XORs 32*s
+  unsigned v[C::kDT];           // V^T operand of dv tile t, key slice 0, V buffer 0
+  unsigned dk[C::kInstPerWave]; // DMA source byte offsets within a key block (K)
+  unsigned dv[C::kInstPerWave]; // (V)
 };
 
 // DMA: instruction t of this wave covers rows inst*kRowsPerInst .. of the block; lane ->
 // (row, physical chunk); the source is the logical chunk that the swizzle places there.  Rows
 // past `row_limit` are clamped to it (only the last, partial block needs that).
-template <int D, int BC>
+template <typename C>
 __device__ __forceinline__ void dma_offsets(unsigned* dk, unsigned* dv, int wave, int lane, int row_limit) {
-  using T = Tile<D, BC>;
+  constexpr int D = C::D;
 #pragma unroll
-  for (int t = 0; t < T::kInstPerWave; ++t) {
-    const int inst = wave * T::kInstPerWave + t;
-    const int r = inst * T::kRowsPerInst + lane / T::kChunksPerRow;
-    const int pc = lane % T::kChunksPerRow;
+  for (int t = 0; t < C::kInstPerWave; ++t) {
+    const int inst = wave * C::kInstPerWave + t;
+    const int r = inst * C::kRowsPerInst + lane / C::kChunksPerRow;
+    const int pc = lane % C::kChunksPerRow;
     const int rr = r < row_limit ? r : row_limit;
     dk[t] = (unsigned)(rr * (D * 2) + ((pc ^ swz_k<D>(r)) * 16));
     dv[t] = (unsigned)(rr * (D * 2) + ((pc ^ swz_v<D>(r)) * 16));
   }
 }
 
-template <int D, int BC>
-__device__ __forceinline__ Lane<D, BC> lane_setup(unsigned smem_base, int wave, int lane) {
-  using T = Tile<D, BC>;
-  Lane<D, BC> a;
+template <typename C>
+__device__ __forceinline__ Lane<C> lane_setup(unsigned smem_base, int wave, int lane) {
+  constexpr int D = C::D;
+  Lane<C> a;
   const int ln = lane & 31, hf = lane >> 5;
   a.k = smem_base + ln * (D * 2) + ((hf ^ swz_k<D>(ln)) * 16);
   const int g = lane >> 4, p = lane & 15;
   const int dvh = g & 1;
   const int r = 4 * hf + (p >> 2);          // row within a 16-key slice, half e = 0
   const int cl = 2 * dvh + ((p & 3) >> 1);  // chunk within a 32-wide dv tile
-  const unsigned base = smem_base + r * (D * 2) + (p & 1) * 8;
+  const unsigned base = smem_base + C::kVBase + r * (D * 2) + (p & 1) * 8;
 #pragma unroll
-  for (int t = 0; t < T::kDT; ++t) a.v[t] = base + (((4 * t + cl) ^ swz_v<D>(r)) * 16);
-  dma_offsets<D, BC>(a.dk, a.dv, wave, lane, BC);
+  for (int t = 0; t < C::kDT; ++t) a.v[t] = base + (((4 * t + cl) ^ swz_v<D>(r)) * 16);
+  dma_offsets<C>(a.dk, a.dv, wave, lane, C::BC);
   return a;
 }
 
-// Issue the DMA of key block `blk` of K (if do_k) and V (if do_v) into buffer `buf`.  The block
-// base is wave-uniform, the per-lane part a 32-bit byte offset.
-template <int D, int BC>
+// Issue the DMA of K block kblk into K buffer kbuf and of V block vblk into V buffer vbuf.  Block
+// bases are wave-uniform, the per-lane parts 32-bit byte offsets.  Every call issues the same
+// number of DMA ops, so vector-memory waits can use fixed counts.
+template <typename C>
 __device__ __forceinline__ void issue_dma(const __bf16* __restrict__ kbase, const __bf16* __restrict__ vbase,
-                                          char* smem, int buf, int blk, int N, int wave, int lane,
-                                          const Lane<D, BC>& la, bool do_k, bool do_v) {
-  using T = Tile<D, BC>;
-  const char* kb = (const char*)(kbase + (int64_t)blk * BC * D);
-  const char* vb = (const char*)(vbase + (int64_t)blk * BC * D);
-  unsigned dk[T::kInstPerWave], dv[T::kInstPerWave];
+                                          char* smem, int kblk, int kbuf, int vblk, int vbuf, int N, int wave,
+                                          int lane, const Lane<C>& la) {
+  constexpr int D = C::D, BC = C::BC;
+  const char* kb = (const char*)(kbase + (int64_t)kblk * BC * D);
+  const char* vb = (const char*)(vbase + (int64_t)vblk * BC * D);
+  unsigned dk[C::kInstPerWave], dv[C::kInstPerWave], tk[C::kInstPerWave], tv[C::kInstPerWave];
 #pragma unroll
-  for (int t = 0; t < T::kInstPerWave; ++t) {
+  for (int t = 0; t < C::kInstPerWave; ++t) {
     dk[t] = la.dk[t];
     dv[t] = la.dv[t];
   }
   // In the last, partial block, rows past N are clamped to N-1: they are masked out of the
   // softmax, and clamping keeps every global address inside the tensors.
-  if (blk * BC + BC > N) dma_offsets<D, BC>(dk, dv, wave, lane, N - 1 - blk * BC);
-  char* kdst = smem + (buf ? T::kKOff1 : T::kKOff0);
-  char* vdst = smem + (buf ? T::kVOff1 : T::kVOff0);
+  if (kblk * BC + BC > N) {
+    dma_offsets<C>(dk, tv, wave, lane, N - 1 - kblk * BC);
+  }
+  if (vblk * BC + BC > N) {
+    dma_offsets<C>(tk, dv, wave, lane, N - 1 - vblk * BC);
+  }
+  char* kdst = smem + kbuf * C::kTensorBytes;
+  char* vdst = smem + C::kVBase + vbuf * C::kTensorBytes;
 #pragma unroll
-  for (int t = 0; t < T::kInstPerWave; ++t) {
-    const int inst = wave * T::kInstPerWave + t;
-    if (do_k)
-      __builtin_amdgcn_global_load_lds((global_cvoid*)(kb + dk[t]), (lds_void*)(kdst + inst * 1024), 16, 0, 0);
-    if (do_v)
-      __builtin_amdgcn_global_load_lds((global_cvoid*)(vb + dv[t]), (lds_void*)(vdst + inst * 1024), 16, 0, 0);
+  for (int t = 0; t < C::kInstPerWave; ++t) {
+    const int inst = wave * C::kInstPerWave + t;
+    __builtin_amdgcn_global_load_lds((global_cvoid*)(kb + dk[t]), (lds_void*)(kdst + inst * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_cvoid*)(vb + dv[t]), (lds_void*)(vdst + inst * 1024), 16, 0, 0);
   }
 }
 
 // ---- the per-wave pipeline stages -------------------------------------------------------------
-template <int D, int BC, bool CAUSAL>
+template <typename C, bool CAUSAL>
 struct Wave {
-  using T = Tile<D, BC>;
+  static constexpr int D = C::D, BC = C::BC;
   static constexpr int kKR = 3;    // K operand ring depth (S^T reads run kKR-1 MFMAs ahead)
-  static constexpr int kVLook = 2; // V^T reads run kVLook PV steps ahead
+  static constexpr int kVLook = 3; // V^T reads run kVLook PV steps ahead
   static constexpr int kVR = 2 * (kVLook + 1);
 
-  bf16x8 qf[T::kDS];
-  f32x16 oacc[T::kDT];
+  bf16x8 qf[C::kDS];
+  f32x16 oacc[C::kDT];
   float m_run;  // running max in log2 units (stale by at most kRescaleSlack)
   float l_run;  // this lane's half of the row sum
   float c;      // |scale| * log2(e), >= 1e-30
   int N, row0, my_row, hf;
-  Lane<D, BC> la;
+  Lane<C> la;
 
   // ---- S^T = K Q^T for one block: step i is d slice i / kKT of key tile i % kKT ----
-  template <int KB, int I>
-  __device__ __forceinline__ void issue_k(bf16x8 (&kr)[kKR], IC<I>) {
-    constexpr int s = I / T::kKT, kt = I % T::kKT;
-    constexpr int off = (KB ? T::kKOff1 : T::kKOff0) + kt * 32 * D * 2;
-    kr[I % kKR] = lds_read_b128<off>(la.k ^ (32u * s));
+  // kaddr is this lane's K address in the block's K buffer.
+  template <int I>
+  __device__ __forceinline__ void issue_k(bf16x8 (&kr)[kKR], unsigned kaddr, IC<I>) {
+    constexpr int s = I / C::kKT, kt = I % C::kKT;
+    kr[I % kKR] = lds_read_b128<kt * 32 * D * 2>(kaddr ^ (32u * s));
   }
-  template <int KB>
-  __device__ __forceinline__ void s_start(bf16x8 (&kr)[kKR]) {
-    [&]<int... I>(std::integer_sequence<int, I...>) { (issue_k<KB>(kr, IC<I>{}), ...); }(
+  __device__ __forceinline__ void s_start(bf16x8 (&kr)[kKR], unsigned kaddr) {
+    [&]<int... I>(std::integer_sequence<int, I...>) { (issue_k(kr, kaddr, IC<I>{}), ...); }(
         std::make_integer_sequence<int, kKR>{});
   }
-  template <int KB, int I>
-  __device__ __forceinline__ void s_step(f32x16 (&sacc)[T::kKT], bf16x8 (&kr)[kKR], IC<I>) {
-    constexpr int n = T::kSSteps;
+  template <int I>
+  __device__ __forceinline__ void s_step(f32x16 (&sacc)[C::kKT], bf16x8 (&kr)[kKR], unsigned kaddr, IC<I>) {
+    constexpr int n = C::kSSteps;
     constexpr int after = (I + kKR < n ? I + kKR : n) - I - 1;  // K reads issued after read I
     lgkm_wait<after>(kr[I % kKR]);
     const bf16x8 a = kr[I % kKR];
-    if constexpr (I + kKR < n) issue_k<KB>(kr, IC<I + kKR>{});
-    constexpr int s = I / T::kKT, kt = I % T::kKT;
+    if constexpr (I + kKR < n) issue_k(kr, kaddr, IC<I + kKR>{});
+    constexpr int s = I / C::kKT, kt = I % C::kKT;
     if constexpr (s == 0)
       sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], (f32x16){}, 0, 0, 0);
     else
       sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kt], 0, 0, 0);
   }
-  template <int KB, int LO, int HI>
-  __device__ __forceinline__ void s_steps(f32x16 (&sacc)[T::kKT], bf16x8 (&kr)[kKR]) {
-    [&]<int... I>(std::integer_sequence<int, I...>) { (s_step<KB>(sacc, kr, IC<LO + I>{}), ...); }(
+  template <int LO, int HI>
+  __device__ __forceinline__ void s_steps(f32x16 (&sacc)[C::kKT], bf16x8 (&kr)[kKR], unsigned kaddr) {
+    [&]<int... I>(std::integer_sequence<int, I...>) { (s_step(sacc, kr, kaddr, IC<LO + I>{}), ...); }(
         std::make_integer_sequence<int, HI - LO>{});
   }
 
   // ---- softmax, part 1: mask (diagonal / tail blocks), block row max, rescale decision ----
-  __device__ __forceinline__ void apply_mask(f32x16 (&sacc)[T::kKT], int key0) {
+  __device__ __forceinline__ void apply_mask(f32x16 (&sacc)[C::kKT], int key0) {
     // Key offset 32kt + 8(i/4) + (i%4) within the block is visible iff it is <= lim.
     int lim = N - 1 - key0 - 4 * hf;
     if (CAUSAL) lim = min(lim, my_row - key0 - 4 * hf);
 #pragma unroll
-    for (int kt = 0; kt < T::kKT; ++kt)
+    for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int off = 32 * kt + 8 * (i >> 2) + (i & 3);
         sacc[kt][i] = off <= lim ? sacc[kt][i] : -__builtin_inff();
       }
   }
-  __device__ __forceinline__ bool softmax_max(const f32x16 (&sacc)[T::kKT], float& bm) {
-    float mx4[2 * T::kKT];
+  __device__ __forceinline__ bool softmax_max(const f32x16 (&sacc)[C::kKT], float& bm) {
+    float mx4[2 * C::kKT];
 #pragma unroll
-    for (int kt = 0; kt < T::kKT; ++kt)
+    for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int i = 8 * h;
@@ -314,7 +326,7 @@ struct Wave {
         m = fmax3(m, sacc[kt][i + 5], sacc[kt][i + 6]);
         mx4[2 * kt + h] = fmax2(m, sacc[kt][i + 7]);
       }
-    static_assert(T::kKT == 2, "row max written for two 32-key tiles");
+    static_assert(C::kKT == 2, "row max written for two 32-key tiles");
     const float mx = half_max(fmax2(fmax3(mx4[0], mx4[1], mx4[2]), mx4[3]));
     bm = mx * c;  // block max in log2 units; c > 0 keeps an all-masked row at -inf
     return bm > m_run + kRescaleSlack;
@@ -325,17 +337,17 @@ struct Wave {
     const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
     l_run *= alpha;
 #pragma unroll
-    for (int t = 0; t < T::kDT; ++t) oacc[t] *= alpha;
+    for (int t = 0; t < C::kDT; ++t) oacc[t] *= alpha;
     m_run = m_new;
   }
 
   // ---- softmax, part 2: P = exp2(S * c - m) packed to bf16, and the row sum ----
   // A masked score is -inf and c > 0, so its weight is exp2(-inf) = 0.
-  __device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[T::kKT], bf16x8 (&pb)[T::kKS]) {
+  __device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[C::kKT], bf16x8 (&pb)[C::kKS]) {
     float ls4[4];
     const float neg_m = -m_run;
 #pragma unroll
-    for (int kt = 0; kt < T::kKT; ++kt)
+    for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][i], c, neg_m));
@@ -348,79 +360,80 @@ struct Wave {
     l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
   }
 
-  // ---- O^T += V^T P^T for one block from V buffer VB ----
+  // ---- O^T += V^T P^T for one block ----
   // Step st multiplies key slice st / kDT into dv tile st % kDT.  Lane (dv row 32t + ln, half hf)
   // needs V[key][dv] for keys 16ks + 4hf + 0..3 (read "lo") and 16ks + 8 + 4hf + 0..3 (read
   // "hi"); the transpose read hands each lane of a 16-lane group its dv column of a 4-key slab.
-  template <int VB, int ST>
-  __device__ __forceinline__ void issue_v(i16x4 (&vr)[kVR], IC<ST>) {
-    constexpr int ks = ST / T::kDT, t = ST % T::kDT;
+  // vbuf is the byte offset of the block's V buffer.
+  template <int ST>
+  __device__ __forceinline__ void issue_v(i16x4 (&vr)[kVR], unsigned vbuf, IC<ST>) {
+    constexpr int ks = ST / C::kDT, t = ST % C::kDT;
     constexpr int slot = ST % (kVLook + 1);
-    constexpr int off = (VB ? T::kVOff1 : T::kVOff0) + ks * 16 * D * 2;
-    vr[2 * slot] = lds_read_tr<off>(la.v[t]);
-    vr[2 * slot + 1] = lds_read_tr<off + 8 * D * 2>(la.v[t]);
+    constexpr int off = ks * 16 * D * 2;
+    vr[2 * slot] = lds_read_tr<off>(la.v[t] + vbuf);
+    vr[2 * slot + 1] = lds_read_tr<off + 8 * D * 2>(la.v[t] + vbuf);
   }
-  template <int VB>
-  __device__ __forceinline__ void pv_start(i16x4 (&vr)[kVR]) {
-    [&]<int... I>(std::integer_sequence<int, I...>) { (issue_v<VB>(vr, IC<I>{}), ...); }(
+  __device__ __forceinline__ void pv_start(i16x4 (&vr)[kVR], unsigned vbuf) {
+    [&]<int... I>(std::integer_sequence<int, I...>) { (issue_v(vr, vbuf, IC<I>{}), ...); }(
         std::make_integer_sequence<int, kVLook>{});
   }
-  template <int VB, int ST>
-  __device__ __forceinline__ void pv_step(const bf16x8 (&pb)[T::kKS], i16x4 (&vr)[kVR], IC<ST>) {
-    constexpr int n = T::kPVSteps;
-    constexpr int ks = ST / T::kDT, t = ST % T::kDT;
+  template <int ST>
+  __device__ __forceinline__ void pv_step(const bf16x8 (&pb)[C::kKS], i16x4 (&vr)[kVR], unsigned vbuf, IC<ST>) {
+    constexpr int n = C::kPVSteps;
+    constexpr int ks = ST / C::kDT, t = ST % C::kDT;
     constexpr int slot = ST % (kVLook + 1);
     constexpr int ahead = (ST + kVLook < n ? ST + kVLook : n) - ST - 1;  // steps issued after this one
     lgkm_wait<2 * ahead>(vr[2 * slot], vr[2 * slot + 1]);
     const i16x8 a16 = __builtin_shufflevector(vr[2 * slot], vr[2 * slot + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-    if constexpr (ST + kVLook < n) issue_v<VB>(vr, IC<ST + kVLook>{});
+    if constexpr (ST + kVLook < n) issue_v(vr, vbuf, IC<ST + kVLook>{});
     // (On the causal diagonal, slices above this wave's rows have all-zero weights; they are
     // multiplied anyway, which keeps this path free of branches.)
     oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16), pb[ks], oacc[t], 0, 0, 0);
   }
-  template <int VB>
-  __device__ __forceinline__ void pv(const bf16x8 (&pb)[T::kKS], i16x4 (&vr)[kVR]) {
-    [&]<int... St>(std::integer_sequence<int, St...>) { (pv_step<VB>(pb, vr, IC<St>{}), ...); }(
-        std::make_integer_sequence<int, T::kPVSteps>{});
+  __device__ __forceinline__ void pv(const bf16x8 (&pb)[C::kKS], i16x4 (&vr)[kVR], unsigned vbuf) {
+    [&]<int... St>(std::integer_sequence<int, St...>) { (pv_step(pb, vr, vbuf, IC<St>{}), ...); }(
+        std::make_integer_sequence<int, C::kPVSteps>{});
   }
 
   // ---- one key block j, with the scores of block j+1 computed alongside ----
-  // `cur` holds S^T(j) on entry and `nxt` holds S^T(j+1) on exit.  K(j+1) is in K buffer
-  // KB = (j+1) & 1 and V(j) in V buffer VB = j & 1.  The first half of the S^T(j+1) MFMAs sits
+  // `cur` holds S^T(j) on entry and `nxt` holds S^T(j+1) on exit.  kbuf / vbuf are the byte
+  // offsets of the buffers holding K(j+1) and V(j).  The first half of the S^T(j+1) MFMAs sits
   // with the row max, the second half with the exponentials, so MFMA and VALU work interleave.
-  // On the last block K buffer KB holds no block and the scores computed from it are unused.
-  template <int KB, int VB>
-  __device__ __forceinline__ void block(f32x16 (&cur)[T::kKT], f32x16 (&nxt)[T::kKT], int key0, bool masked) {
+  // On the last block the K buffer holds no new block and the scores computed from it are
+  // unused.
+  __device__ __forceinline__ void block(f32x16 (&cur)[C::kKT], f32x16 (&nxt)[C::kKT], int key0, bool masked,
+                                        unsigned kbuf, unsigned vbuf) {
     bf16x8 kr[kKR];
-    constexpr int half = T::kSSteps / 2;
+    constexpr int half = C::kSSteps / 2;
+    const unsigned kaddr = la.k + kbuf;
     if (masked) apply_mask(cur, key0);
-    s_start<KB>(kr);
-    s_steps<KB, 0, half>(nxt, kr);
+    s_start(kr, kaddr);
+    s_steps<0, half>(nxt, kr, kaddr);
     float bm;
     const bool grow = softmax_max(cur, bm);
     if (__builtin_amdgcn_ballot_w64(grow)) rescale(grow, bm);
-    bf16x8 pb[T::kKS];
-    s_steps<KB, half, T::kSSteps>(nxt, kr);
+    bf16x8 pb[C::kKS];
+    s_steps<half, C::kSSteps>(nxt, kr, kaddr);
     softmax_exp(cur, pb);
     i16x4 vr[kVR];
-    pv_start<VB>(vr);
-    pv<VB>(pb, vr);
+    pv_start(vr, vbuf);
+    pv(pb, vr, vbuf);
   }
 
-  // Scores of the first block (no softmax to overlap with).
-  __device__ __forceinline__ void first_scores(f32x16 (&s)[T::kKT]) {
+  // Scores of the first block (no softmax to overlap with); K(0) is in K buffer 0.
+  __device__ __forceinline__ void first_scores(f32x16 (&s)[C::kKT]) {
     bf16x8 kr[kKR];
-    s_start<0>(kr);
-    s_steps<0, 0, T::kSSteps>(s, kr);
+    s_start(kr, la.k);
+    s_steps<0, C::kSSteps>(s, kr, la.k);
   }
 };
 
-template <int D, int BC, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+template <typename C, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(C::kThreads, C::kThreads), amdgpu_waves_per_eu(2, 2)))
 void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      const __bf16* __restrict__ v, float* __restrict__ o, float* __restrict__ lse,
                      int N, int BH, int n_qtiles, float c_log2, int negate_q, int xcd_group) {
-  using T = Tile<D, BC>;
+  constexpr int D = C::D, BC = C::BC, NBUF = C::NBUF, kBR = C::kBR;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int tid = threadIdx.x;
@@ -452,7 +465,7 @@ void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const __bf16* __restrict__ kh = k + head_off;
   const __bf16* __restrict__ vh = v + head_off;
 
-  Wave<D, BC, CAUSAL> W;
+  Wave<C, CAUSAL> W;
   W.N = N;
   W.row0 = qt * kBR + wave * kRowsPerWave;
   W.my_row = W.row0 + ln;
@@ -461,14 +474,14 @@ void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   W.m_run = -__builtin_inff();
   W.l_run = 0.f;
 #pragma unroll
-  for (int t = 0; t < T::kDT; ++t) W.oacc[t] = (f32x16){};
+  for (int t = 0; t < C::kDT; ++t) W.oacc[t] = (f32x16){};
 
   // ---- Q rows into VGPRs (B operand of S^T = K Q^T: lane holds q[row][16s + 8hf .. +7]) ----
   {
     const int r = W.my_row < N ? W.my_row : N - 1;
     const __bf16* src = qh + (int64_t)r * D + 8 * hf;
 #pragma unroll
-    for (int s = 0; s < T::kDS; ++s) {
+    for (int s = 0; s < C::kDS; ++s) {
       u32x4 raw = *(const u32x4*)(src + 16 * s);
       if (negate_q) raw ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
       W.qf[s] = __builtin_bit_cast(bf16x8, raw);
@@ -487,33 +500,46 @@ void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 
   const unsigned smem_base = (unsigned)(uintptr_t)(lds_void*)smem;
-  W.la = lane_setup<D, BC>(smem_base, wave, lane);
+  W.la = lane_setup<C>(smem_base, wave, lane);
 
-  // ---- prologue: K(0), V(0) and K(1) in flight; scores of block 0 ----
-  issue_dma<D, BC>(kh, vh, smem, 0, 0, N, wave, lane, W.la, true, true);
-  if (nblk > 1) issue_dma<D, BC>(kh, vh, smem, 1, 1, N, wave, lane, W.la, true, false);
-  wait_vmcnt0();
+  // ---- DMA schedule ----
+  // K(i) lives in K buffer i % NBUF and V(i) in V buffer i % NBUF.  Group g (issued at block g,
+  // after its barrier) loads K(g + NBUF) and V(g + NBUF - 1) into the buffers that blocks g and
+  // g - 1 have just released; block indices past the end are clamped to the last block, so every
+  // group has the same size.  Block j needs K(j+1) and V(j), which group j + 1 - NBUF loaded;
+  // NBUF - 2 groups have been issued since.
+  const int last = nblk - 1;
+  auto group = [&](int g) {
+    const int kb = min(g + NBUF, last), vb = min(g + NBUF - 1, last);
+    issue_dma<C>(kh, vh, smem, kb, (g + NBUF) % NBUF, vb, (g + NBUF - 1) % NBUF, N, wave, lane, W.la);
+  };
+  // Prologue: K(0) with V(0) into buffers 0, then groups -(NBUF-1) .. -1 (for NBUF = 2 that is
+  // group -1: K(1), V(0) again into V buffer 0).
+  issue_dma<C>(kh, vh, smem, 0, 0, 0, 0, N, wave, lane, W.la);
+  for (int g = 1 - NBUF; g < 0; ++g) group(g);
+  wait_vmcnt<(NBUF - 1) * C::kDmaPerGroup>();  // K(0) has landed
   __builtin_amdgcn_s_barrier();
 
-  f32x16 sA[T::kKT], sB[T::kKT];
+  f32x16 sA[C::kKT], sB[C::kKT];
   W.first_scores(sA);
 
-  // ---- main loop, unrolled by two so buffer parities are compile-time ----
-  // At block j: wait for K(j+1) and V(j), barrier (every wave is done with block j-1, whose
-  // buffers are the ones refilled next), issue K(j+2) and V(j+1), then the block itself.
-  auto step = [&](auto par_c, int j, f32x16(&cur)[T::kKT], f32x16(&nxt)[T::kKT]) {
-    constexpr int P = decltype(par_c)::value;  // j & 1
-    wait_vmcnt0();
-    __builtin_amdgcn_s_barrier();
-    if (j + 2 < nblk) issue_dma<D, BC>(kh, vh, smem, P, j + 2, N, wave, lane, W.la, true, false);
-    if (j + 1 < nblk) issue_dma<D, BC>(kh, vh, smem, P ^ 1, j + 1, N, wave, lane, W.la, false, true);
-    W.template block<P ^ 1, P>(cur, nxt, j * BC, j >= j_mask);
+  // ---- main loop, unrolled by two so the score registers alternate roles statically ----
+  auto step = [&](int j, f32x16(&cur)[C::kKT], f32x16(&nxt)[C::kKT]) {
+    wait_vmcnt<(NBUF - 2) * C::kDmaPerGroup>();  // K(j+1) and V(j) have landed
+    __builtin_amdgcn_s_barrier();                // ... for every wave; block j-1 is done
+    group(j);
+    const unsigned kbuf = (unsigned)(((j + 1) % NBUF) * C::kTensorBytes);
+    const unsigned vbuf = (unsigned)((j % NBUF) * C::kTensorBytes);
+    W.block(cur, nxt, j * BC, j >= j_mask, kbuf, vbuf);
   };
   for (int j = 0; j < nblk; j += 2) {
-    step(IC<0>{}, j, sA, sB);
+    step(j, sA, sB);
     if (j + 1 >= nblk) break;
-    step(IC<1>{}, j + 1, sB, sA);
+    step(j + 1, sB, sA);
   }
+  // The trailing groups only reloaded the last block; let them land before the workgroup's
+  // LDS can be handed to another workgroup.
+  wait_vmcnt<0>();
 
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ----
   const float l_tot = half_sum(W.l_run);
@@ -521,7 +547,7 @@ void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
     const float inv = 1.f / l_tot;
     float* orow = o + head_off + (int64_t)W.my_row * D;
 #pragma unroll
-    for (int t = 0; t < T::kDT; ++t)
+    for (int t = 0; t < C::kDT; ++t)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         f32x4 val = {W.oacc[t][4 * g4] * inv, W.oacc[t][4 * g4 + 1] * inv, W.oacc[t][4 * g4 + 2] * inv,
@@ -532,11 +558,10 @@ void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   }
 }
 
-template <int D, int BC, bool CAUSAL>
+template <typename C, bool CAUSAL>
 hipError_t launch(const void* q, const void* k, const void* v, float* o, float* lse, int N, int BH,
                   float scale, hipStream_t stream) {
-  using T = Tile<D, BC>;
-  const int n_qtiles = (N + kBR - 1) / kBR;
+  const int n_qtiles = (N + C::kBR - 1) / C::kBR;
   const int64_t tiles = (int64_t)BH * n_qtiles;
   const int xcd_group = (BH % kXcds == 0) ? 1 : 0;
   const int negate_q = scale < 0.f ? 1 : 0;
@@ -546,15 +571,26 @@ hipError_t launch(const void* q, const void* k, const void* v, float* o, float* 
   double c_exact = (double)(negate_q ? -scale : scale) * 1.4426950408889634;
   if (c_exact < 1e-30) c_exact = 1e-30;
   const float c_log2 = (float)c_exact;
-  auto kern = mifa_fwd_kernel<D, BC, CAUSAL>;
+  auto kern = mifa_fwd_kernel<C, CAUSAL>;
   // Raise the dynamic-LDS limit once per instantiation (thread-safe static initialisation).
   static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, T::kLdsBytes);
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(kThreads), T::kLdsBytes, stream,
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::kThreads), C::kLdsBytes, stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, o, lse, N, BH, n_qtiles, c_log2,
                      negate_q, xcd_group);
   return hipGetLastError();
+}
+
+// Launch-shape choice: 8-wave workgroups (256 rows, one per CU) when there are at least as many
+// of them as CUs, else 4-wave workgroups (128 rows, two per CU) to fill the machine.
+constexpr int kCUs = 256;
+template <int D, bool CAUSAL>
+hipError_t dispatch(const void* q, const void* k, const void* v, float* o, float* lse, int N, int BH,
+                    float scale, hipStream_t stream) {
+  const int64_t big_tiles = (int64_t)BH * ((N + 255) / 256);
+  if (big_tiles >= kCUs) return launch<Cfg<D, 64, 8, 3>, CAUSAL>(q, k, v, o, lse, N, BH, scale, stream);
+  return launch<Cfg<D, 64, 4, 2>, CAUSAL>(q, k, v, o, lse, N, BH, scale, stream);
 }
 
 thread_local int g_last_hip_error = 0;
@@ -575,17 +611,17 @@ int mifa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, 
   if (N * d >= ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
   if (B > ((int64_t)1 << 31) || H > ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
   const int64_t BH = B * H;
-  const int64_t tiles = BH * ((N + kBR - 1) / kBR);
+  const int64_t tiles = BH * ((N + 127) / 128);
   if (BH >= ((int64_t)1 << 31) || tiles >= ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
 
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (d == 128)
-    e = causal ? launch<128, 64, true>(q, k, v, o, lse, (int)N, (int)BH, scale, s)
-               : launch<128, 64, false>(q, k, v, o, lse, (int)N, (int)BH, scale, s);
+    e = causal ? dispatch<128, true>(q, k, v, o, lse, (int)N, (int)BH, scale, s)
+               : dispatch<128, false>(q, k, v, o, lse, (int)N, (int)BH, scale, s);
   else
-    e = causal ? launch<64, 64, true>(q, k, v, o, lse, (int)N, (int)BH, scale, s)
-               : launch<64, 64, false>(q, k, v, o, lse, (int)N, (int)BH, scale, s);
+    e = causal ? dispatch<64, true>(q, k, v, o, lse, (int)N, (int)BH, scale, s)
+               : dispatch<64, false>(q, k, v, o, lse, (int)N, (int)BH, scale, s);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return MIFA_ERR_HIP;

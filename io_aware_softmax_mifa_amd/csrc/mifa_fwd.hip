@@ -46,6 +46,8 @@
 //    masking code; all other blocks take a mask-free path.
 //  * LDS tiles are XOR-swizzled in 16-byte chunks to spread the K reads and the V transpose
 //    reads over the banks.
+//  * The first half of the waves run at a raised issue priority, so the two waves sharing a
+//    SIMD drift out of step and their MFMA-only and VALU-heavy stretches overlap.
 //  * Grid: one workgroup per (b, h, q-tile), heaviest causal tiles first, and when the tile
 //    count allows it, all tiles of one head are placed on the same XCD (workgroups are handed
 //    to the 8 XCDs round-robin) so K/V re-reads hit that XCD's L2.
@@ -259,8 +261,8 @@ __device__ __forceinline__ void issue_dma(const __bf16* __restrict__ kbase, cons
 template <typename C, bool CAUSAL>
 struct Wave {
   static constexpr int D = C::D, BC = C::BC;
-  static constexpr int kKR = 3;    // K operand ring depth (S^T reads run kKR-1 MFMAs ahead)
-  static constexpr int kVLook = 3; // V^T reads run kVLook PV steps ahead
+  static constexpr int kKR = 6;    // K operand ring depth (S^T reads run kKR-1 MFMAs ahead)
+  static constexpr int kVLook = 8; // V^T reads run kVLook PV steps ahead
   static constexpr int kVR = 2 * (kVLook + 1);
 
   bf16x8 qf[C::kDS];
@@ -501,6 +503,10 @@ void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
   const unsigned smem_base = (unsigned)(uintptr_t)(lds_void*)smem;
   W.la = lane_setup<C>(smem_base, wave, lane);
+  // The two waves that share a SIMD run the same block in step (one barrier per block).  A
+  // static priority for the first half of the waves lets one of them run ahead, so that its
+  // MFMA-only stretches (PV) line up with the other's VALU-heavy ones (softmax).
+  if (wave < C::WAVES / 2) __builtin_amdgcn_s_setprio(1);
 
   // ---- DMA schedule ----
   // K(i) lives in K buffer i % NBUF and V(i) in V buffer i % NBUF.  Group g (issued at block g,

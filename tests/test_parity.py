@@ -87,6 +87,29 @@ def test_large_configs_sampled(name):
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
+# ---- the long-sequence launch shape (8-wave workgroups, four K/V buffers) ----------------
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dist", ["normal", "stress"])
+def test_long_sequence_launch_shape(d, causal, dist):
+    """N > 4096 with at least 256 workgroups of 256 rows takes the 8-wave launch; N = 4133 also
+    ends in a partial key block.  Two whole heads and 128 sampled rows against the oracle."""
+    B, H, N = 1, 16, 4133
+    q, k, v = W.make_inputs(B, H, N, d, seed=4133 + d, dist=dist)
+    scale = W.fp32_scale(d)
+    say(f"long: B={B} H={H} N={N} d={d} causal={causal} dist={dist}")
+    o, lse = run_gpu(q, k, v, causal, scale)
+    for h in (0, H - 1):
+        ho, hl = attention_fp64(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], causal=causal, scale=scale)
+        check(o[:, h:h + 1], lse[:, h:h + 1], ho, hl, f"long d={d} causal={causal} {dist} head {h}")
+    rows = W.sample_rows(B, H, N, 128, seed=d + 7)
+    ro, rl = attention_fp64_rows(q, k, v, rows, causal=causal, scale=scale)
+    r = rows.numpy()
+    check(o[r[:, 0], r[:, 1], r[:, 2]].double().numpy(), lse[r[:, 0], r[:, 1], r[:, 2]].double().numpy(), ro, rl,
+          f"long d={d} causal={causal} {dist} sampled rows")
+
+
 # ---- ragged and tiny sequence lengths --------------------------------------------------
 
 @pytest.mark.parametrize("d", [64, 128])

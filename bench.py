@@ -9,6 +9,10 @@ the timed region.  Prints ONE JSON line on stdout.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C4] [--no-cpu-baseline]
 
 FLOPs per step follow the usual attention convention: 4*B*H*N^2*d, halved for causal.
+
+`--workload SM1` .. `SM4` time the stand-alone row softmax (mifa_softmax_rows) instead: one
+step is one launch over a [rows, cols] matrix, and the metric is HBM throughput of the
+compulsory bytes (the input read once, the output and the row LSE written once).
 """
 from __future__ import annotations
 
@@ -27,6 +31,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 KERNEL_SOURCE = os.path.join(ROOT, "io_aware_softmax_mifa_amd", "csrc", "mifa_fwd.hip")
+SOFTMAX_SOURCE = os.path.join(ROOT, "io_aware_softmax_mifa_amd", "csrc", "mifa_softmax.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -45,21 +50,24 @@ def compulsory_bytes(w) -> int:
     return 3 * 2 * n * w.d + 4 * n * w.d + 4 * n
 
 
-def kernel_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def kernel_sha(source: str = KERNEL_SOURCE) -> str:
+    with open(source, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, source: str = KERNEL_SOURCE):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
-    counters were taken on another kernel source or another workload."""
+    counters were taken on another kernel source or another workload.  An entry may carry its
+    own source hash (other kernels than the attention forward)."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     entry = t.get("workloads", {}).get(workload)
-    if not entry or t.get("kernel_source_sha256") != kernel_sha():
+    if not entry:
+        return None
+    if entry.get("kernel_source_sha256", t.get("kernel_source_sha256")) != kernel_sha(source):
         return None
     return entry.get("traffic_bytes")
 
@@ -100,6 +108,123 @@ def cpu_baseline(w, q, k, v, scale, rows_count: int):
     }
 
 
+def copy_calibration(dev):
+    """A plain device-to-device copy of 1 GiB, three times: its FETCH_SIZE / WRITE_SIZE counters
+    give the scale from counter units to bytes."""
+    import torch
+
+    n = 1 << 29
+    a = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 3 copies of {2 * n} bytes")
+    del a, b
+
+
+def softmax_bytes(w) -> int:
+    """Compulsory bytes of one row-softmax launch: x read once, y and lse written once."""
+    return 2 * w.rows * w.cols * w.element_bytes + 4 * w.rows
+
+
+def softmax_cpu_baseline(w, x, rows_count: int):
+    """The float64 softmax oracle as it stands, on a bounded seeded sample of rows."""
+    from io_aware_softmax_mifa_amd import workloads as W
+    from oracle import softmax_rows_fp64
+
+    rows = W.sample_softmax_rows(w.rows, rows_count, w.seed + 7)
+    sample = x[rows]
+    t0 = time.perf_counter()
+    softmax_rows_fp64(sample, w.scale)
+    dt = time.perf_counter() - t0
+    per_row = softmax_bytes(w) / w.rows
+    return {
+        "value": rows.shape[0] * per_row / dt / 1e9,
+        "unit": "GB/s",
+        "cores": blas_threads(),
+        "kind": "oracle",
+        "sample": (f"{rows.shape[0]} seeded rows of the same workload (float64 NumPy oracle), {dt:.2f} s; "
+                   f"credited {per_row:.0f} compulsory bytes per row"),
+        "seconds": dt,
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def bench_softmax(args):
+    import torch
+
+    from io_aware_softmax_mifa_amd import binding
+    from io_aware_softmax_mifa_amd import workloads as W
+
+    w = W.softmax_by_name(args.workload)
+    log(f"workload {w.name}: rows={w.rows} cols={w.cols} dtype={w.dtype} std={w.std}")
+    x = W.make_softmax_input(w.rows, w.cols, w.dtype, w.std, w.seed)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dx = x.to(dev)
+    y = torch.empty_like(dx)
+    lse = torch.empty(w.rows, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    dtype = binding.MIFA_DTYPE_BF16 if w.dtype == "bf16" else binding.MIFA_DTYPE_F32
+
+    def step():
+        binding.mifa_softmax_rows(dx, y, lse, w.rows, w.cols, dtype, w.scale, stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kernel_ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / args.steps
+    nbytes = softmax_bytes(w)
+    if args.copy_calibration:
+        copy_calibration(dev)
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {kernel_ms:.4f} ms/launch (HIP events)")
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    out = {
+        "metric": "row softmax HBM throughput (compulsory bytes) and % of MI355X HBM bandwidth",
+        "value": nbytes / (ms_per_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "data": "synthetic (seeded i.i.d. normal rows)",
+        "config": {
+            "workload": f"{w.name}: rows={w.rows} cols={w.cols} {w.dtype} x ~ N(0, {w.std:g}^2), scale {w.scale:g}; "
+                        f"y same dtype + fp32 LSE",
+            "rows": w.rows, "cols": w.cols, "element": w.dtype,
+            "compulsory_hbm_bytes": nbytes,
+            "kernel_ms": kernel_ms,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": measured_traffic(w.name, SOFTMAX_SOURCE),
+        },
+    }
+    out["cpu_baseline"] = None if args.no_cpu_baseline else softmax_cpu_baseline(w, x, args.cpu_rows_softmax)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,6 +233,7 @@ def main():
     ap.add_argument("--workload", default="C4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=131072)
+    ap.add_argument("--cpu-rows-softmax", type=int, default=16384)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter calibration)")
     args = ap.parse_args()
@@ -117,6 +243,9 @@ def main():
               "multi-GPU path: heads shard across GPUs with no communication, so the per-GPU figure is the "
               "one-GPU run on that GPU's share).", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload.startswith("SM"):
+        return bench_softmax(args)
 
     import torch
 
@@ -162,17 +291,7 @@ def main():
     cb = compulsory_bytes(w)
 
     if args.copy_calibration:
-        # A plain device-to-device copy of 1 GiB: its FETCH_SIZE / WRITE_SIZE counters give the
-        # scale from counter units to bytes.
-        n = 1 << 29
-        a = torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        log(f"copy calibration: 3 copies of {2 * n} bytes")
-        del a, b
+        copy_calibration(dev)
 
     out = {
         "metric": "attention fwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak",

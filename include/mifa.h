@@ -18,7 +18,7 @@
  * partial results over disjoint key sets be merged.
  *
  * Conventions for every entry point:
- *   - Pointers named q, k, v, o, lse are DEVICE pointers (hipMalloc'd or equivalent) on
+ *   - Pointers named q, k, v, o, lse, x, y are DEVICE pointers (hipMalloc'd or equivalent) on
  *     the current HIP device.  The caller allocates and owns them; the library allocates
  *     nothing, keeps no pointer after returning and has no mutable global state, so calls
  *     are thread-safe and re-entrant.
@@ -45,8 +45,15 @@ typedef enum mifa_status {
   MIFA_ERR_MISALIGNED = 4,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   MIFA_ERR_BAD_SCALE = 5,      /* scale is NaN or infinite */
   MIFA_ERR_TOO_LARGE = 6,      /* N*d >= 2^31, or B*H*ceil(N/128) >= 2^31 work tiles */
-  MIFA_ERR_HIP = 7             /* the HIP runtime rejected the launch; see mifa_last_hip_error */
+  MIFA_ERR_HIP = 7,            /* the HIP runtime rejected the launch; see mifa_last_hip_error */
+  MIFA_ERR_BAD_DTYPE = 8       /* dtype is not one of mifa_dtype (mifa_softmax_rows) */
 } mifa_status;
+
+/* Element types of mifa_softmax_rows. */
+typedef enum mifa_dtype {
+  MIFA_DTYPE_BF16 = 0,         /* bfloat16 bit patterns, 2 bytes */
+  MIFA_DTYPE_F32 = 1           /* IEEE float32, 4 bytes */
+} mifa_dtype;
 
 /*
  * mifa_fwd -- exact attention forward, FlashAttention style.
@@ -71,6 +78,43 @@ typedef enum mifa_status {
 int mifa_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
              int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
              void* stream);
+
+/*
+ * mifa_softmax_rows -- the row softmax on its own, with the online normaliser.
+ *
+ * For every row r of X and s_rj = scale * x_rj:
+ *
+ *     y_rj  = exp(s_rj - m_r) / l_r,   m_r = max_j s_rj,   l_r = sum_j exp(s_rj - m_r)
+ *     lse_r = m_r + ln l_r
+ *
+ * This is the online-softmax trick of the interview "Tri Dao: prediction" (transcript) taken
+ * by itself: the maximum and the sum come from one pass over the row, the sum being rescaled
+ * whenever the running maximum grows, and a second pass normalises.  Rows of up to 32,768
+ * elements are read from memory once (they stay on chip between the passes).
+ *
+ *   x      device pointer, `rows` rows of `cols` elements of type `dtype`, contiguous, the
+ *          column index fastest: element (r, j) at r*cols + j.  Read only.  An entry equal to
+ *          -inf takes no weight (for every scale); each row needs at least one finite entry
+ *          (a row of -inf only gives unspecified values).  Other entries must be finite.
+ *   y      device pointer, same shape and type, fully overwritten.  y may equal x (in place);
+ *          any other overlap is undefined.  bf16 outputs are rounded to nearest even.
+ *   lse    device pointer to `rows` float32 values, fully overwritten; or NULL to skip it.
+ *   rows, cols  each >= 1 and < 2^31.
+ *   dtype  MIFA_DTYPE_BF16 or MIFA_DTYPE_F32 (for both x and y).
+ *   scale  multiplies x before the softmax; any finite value, including 0 and negatives.
+ *   stream hipStream_t (as void*); NULL for the null stream.
+ *
+ * Alignment: x and y aligned to the element size, lse to 4 bytes (MIFA_ERR_MISALIGNED
+ * otherwise).  16-byte aligned bases with rows a multiple of 16 bytes take vector loads.
+ * Errors, in order: MIFA_ERR_NULL_POINTER (x or y NULL), MIFA_ERR_BAD_SHAPE,
+ * MIFA_ERR_BAD_DTYPE, MIFA_ERR_MISALIGNED, MIFA_ERR_BAD_SCALE, MIFA_ERR_TOO_LARGE,
+ * MIFA_ERR_HIP.  Ownership, streams and threading as for every entry point (see the top of
+ * this file).
+ * Accuracy: fp32 arithmetic (exp2 with scale*log2(e) folded in); about 1e-6 relative for
+ * fp32 outputs, one bf16 rounding for bf16 outputs.
+ */
+int mifa_softmax_rows(const void* x, void* y, float* lse, int64_t rows, int64_t cols, int dtype,
+                      float scale, void* stream);
 
 /* Human-readable name of a status code; never NULL (unknown codes give "unknown status"). */
 const char* mifa_status_string(int status);

@@ -1,6 +1,7 @@
 """Thin ctypes binding of libmifa (C ABI in include/mifa.h).
 
-Argument marshalling only: every step of attention runs in the HIP library.  torch supplies
+Argument marshalling only: every step of attention and of the row softmax runs in the HIP
+library.  torch supplies
 device memory and the current stream.  If the library is missing this module raises at import
 time; there is no CPU fallback.
 """
@@ -24,8 +25,10 @@ STATUS_NAMES = {
     5: "MIFA_ERR_BAD_SCALE",
     6: "MIFA_ERR_TOO_LARGE",
     7: "MIFA_ERR_HIP",
+    8: "MIFA_ERR_BAD_DTYPE",
 }
-EXPORTED = ("mifa_fwd", "mifa_status_string", "mifa_version", "mifa_last_hip_error")
+MIFA_DTYPE_BF16, MIFA_DTYPE_F32 = 0, 1
+EXPORTED = ("mifa_fwd", "mifa_softmax_rows", "mifa_status_string", "mifa_version", "mifa_last_hip_error")
 
 
 class MifaError(RuntimeError):
@@ -43,6 +46,9 @@ def _load() -> ctypes.CDLL:
     lib.mifa_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_float,
                                                                              ctypes.c_void_p]
     lib.mifa_fwd.restype = ctypes.c_int
+    lib.mifa_softmax_rows.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_float,
+                                                                                      ctypes.c_void_p]
+    lib.mifa_softmax_rows.restype = ctypes.c_int
     lib.mifa_status_string.argtypes = [ctypes.c_int]
     lib.mifa_status_string.restype = ctypes.c_char_p
     lib.mifa_version.argtypes = []
@@ -135,4 +141,54 @@ def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = 
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
     with torch.cuda.device(q.device):
         mifa_fwd(q, k, v, out, lse, B, H, N, d, causal, scale, torch.cuda.current_stream(q.device).cuda_stream)
+    return out, lse
+
+
+# ---- the row softmax ------------------------------------------------------------------------
+
+_DTYPES = {torch.bfloat16: MIFA_DTYPE_BF16, torch.float32: MIFA_DTYPE_F32}
+
+
+def mifa_softmax_rows_raw(x, y, lse, rows, cols, dtype, scale, stream) -> int:
+    """Call the C entry point with raw integer pointers or tensors; returns the status code."""
+    return int(_lib.mifa_softmax_rows(_ptr(x), _ptr(y), _ptr(lse), int(rows), int(cols), int(dtype), float(scale),
+                                      stream or None))
+
+
+def mifa_softmax_rows(x, y, lse, rows, cols, dtype, scale, stream=None) -> None:
+    """Same arguments as the C function; tensors or integer device pointers.  Raises MifaError."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = mifa_softmax_rows_raw(x, y, lse, rows, cols, dtype, scale, stream)
+    if st != MIFA_OK:
+        extra = f" (hipError {mifa_last_hip_error()})" if st == 7 else ""
+        raise MifaError(st, mifa_status_string(st) + extra)
+
+
+def softmax_rows(x: torch.Tensor, scale: float = 1.0, out: torch.Tensor | None = None,
+                 lse: torch.Tensor | None = None, with_lse: bool = True):
+    """Softmax over the last dimension of a contiguous bf16 or fp32 GPU tensor.
+
+    Returns (y, lse): y like x (same dtype), lse float32 over the leading dimensions (None when
+    with_lse is False).  `out` may be x itself (in place).  Asynchronous on the current stream."""
+    if not isinstance(x, torch.Tensor) or x.device.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    if x.dtype not in _DTYPES:
+        raise ValueError(f"x must be bfloat16 or float32, got {x.dtype}")
+    if x.dim() < 1 or x.numel() == 0 or not x.is_contiguous():
+        raise ValueError("x must be a non-empty contiguous tensor")
+    cols = x.shape[-1]
+    rows = x.numel() // cols
+    if out is None:
+        out = torch.empty_like(x)
+    if out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous() or out.device != x.device:
+        raise ValueError("out must be a contiguous tensor like x on x's device")
+    if with_lse and lse is None:
+        lse = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    if lse is not None and (lse.numel() != rows or lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or lse.device != x.device):
+        raise ValueError("lse must be a contiguous float32 tensor with one value per row on x's device")
+    with torch.cuda.device(x.device):
+        mifa_softmax_rows(x, out, lse, rows, cols, _DTYPES[x.dtype], scale,
+                          torch.cuda.current_stream(x.device).cuda_stream)
     return out, lse

@@ -690,6 +690,7 @@ const char* mifa_status_string(int status) {
     case MIFA_ERR_BAD_SCALE: return "scale must be finite";
     case MIFA_ERR_TOO_LARGE: return "problem too large (N*d or the tile count reaches 2^31)";
     case MIFA_ERR_HIP: return "HIP runtime error (see mifa_last_hip_error)";
+    case MIFA_ERR_BAD_DTYPE: return "dtype must be MIFA_DTYPE_BF16 or MIFA_DTYPE_F32";
     default: return "unknown status";
   }
 }
@@ -697,5 +698,7 @@ const char* mifa_status_string(int status) {
 const char* mifa_version(void) { return "mifa 0.1.0 gfx950"; }
 
 int mifa_last_hip_error(void) { return g_last_hip_error; }
+
+__attribute__((visibility("hidden"))) void mifa_record_hip_error(int e) { g_last_hip_error = e; }
 
 }  // extern "C"

@@ -17,7 +17,8 @@ import math
 
 import torch
 
-__all__ = ["Workload", "CONFIGS", "by_name", "fp32_scale", "make_inputs", "sample_rows"]
+__all__ = ["Workload", "CONFIGS", "by_name", "fp32_scale", "make_inputs", "sample_rows", "SoftmaxWorkload",
+           "SOFTMAX_CONFIGS", "softmax_by_name", "make_softmax_input", "sample_softmax_rows"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -111,3 +112,71 @@ def sample_rows(B: int, H: int, N: int, count: int, seed: int) -> torch.Tensor:
     flat = torch.tensor(chosen, dtype=torch.int64)
     bh, i = flat // N, flat % N
     return torch.stack([bh // H, bh % H, i], dim=1)
+
+
+# ---- row-softmax workloads -------------------------------------------------------------------
+# Stand-ins for the score rows the online-softmax trick normalises: a row is one query's
+# scores over the keys, i.i.d. normal with the stated standard deviation (1 for unit-scale
+# logits, 4 for the large-logit case), drawn in float32 from a seeded CPU generator and, for
+# bf16, rounded to nearest even.
+
+@dataclasses.dataclass(frozen=True)
+class SoftmaxWorkload:
+    name: str
+    rows: int
+    cols: int
+    dtype: str     # "bf16" or "f32"
+    std: float
+    seed: int
+    scale: float = 1.0
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    @property
+    def element_bytes(self) -> int:
+        return 2 if self.dtype == "bf16" else 4
+
+
+SOFTMAX_CONFIGS = [
+    # the score matrix of the B=8 H=16 N=2048 attention (rows = B*H*N queries, cols = N keys)
+    SoftmaxWorkload("SM1", 8 * 16 * 2048, 2048, "bf16", 1.0, 201),
+    # the longest rows kept in registers, large logits
+    SoftmaxWorkload("SM2", 4096, 32768, "bf16", 4.0, 202),
+    # long rows, fp32
+    SoftmaxWorkload("SM3", 4096, 16384, "f32", 2.0, 203),
+    # short rows whose length is no multiple of 16 bytes (element loads), fp32
+    SoftmaxWorkload("SM4", 65536, 1001, "f32", 1.0, 204),
+    # rows longer than LDS holds (streamed: read twice)
+    SoftmaxWorkload("SM5", 1024, 131072, "bf16", 1.0, 205),
+]
+
+
+def softmax_by_name(name: str) -> SoftmaxWorkload:
+    for w in SOFTMAX_CONFIGS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def make_softmax_input(rows: int, cols: int, dtype: str, std: float, seed: int) -> torch.Tensor:
+    """A [rows, cols] CPU tensor of i.i.d. N(0, std^2) values in bf16 or fp32."""
+    g = torch.Generator().manual_seed(seed)
+    x = std * torch.randn((rows, cols), generator=g)
+    return x.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+def sample_softmax_rows(rows: int, count: int, seed: int) -> torch.Tensor:
+    """Distinct seeded row indices (always including the first and last row), int64."""
+    g = torch.Generator().manual_seed(seed + 2000)
+    count = min(count, rows)
+    chosen = sorted({0, rows - 1})[:count]
+    taken = set(chosen)
+    for r in torch.randperm(rows, generator=g).tolist():
+        if len(chosen) >= count:
+            break
+        if r not in taken:
+            taken.add(r)
+            chosen.append(r)
+    return torch.tensor(chosen, dtype=torch.int64)

@@ -21,7 +21,8 @@ def declared_functions():
 
 
 def test_header_declares_expected_api():
-    assert declared_functions() == ["mifa_fwd", "mifa_last_hip_error", "mifa_status_string", "mifa_version"]
+    assert declared_functions() == ["mifa_fwd", "mifa_last_hip_error", "mifa_softmax_rows", "mifa_status_string",
+                                    "mifa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -41,7 +42,7 @@ def lib():
 def test_version_and_status_strings(lib):
     assert lib.mifa_version().startswith("mifa ")
     assert "gfx950" in lib.mifa_version()
-    for code in range(8):
+    for code in range(9):
         s = lib.mifa_status_string(code)
         assert s and s != "unknown status"
     assert lib.mifa_status_string(99) == "unknown status"
@@ -98,3 +99,47 @@ def test_binding_python_checks(lib):
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         lib.attention(q, q, q)  # CPU tensors are rejected before any call
+
+
+# ---- mifa_softmax_rows ------------------------------------------------------------------------
+
+@pytest.mark.parametrize(
+    "args,status",
+    [
+        ((0, A, A, 4, 64, 0, 1.0), 1),
+        ((A, 0, A, 4, 64, 0, 1.0), 1),
+        ((A, A, A, 0, 64, 0, 1.0), 2),
+        ((A, A, A, 4, 0, 1, 1.0), 2),
+        ((A, A, A, -1, 64, 0, 1.0), 2),
+        ((A, A, A, 4, 64, 2, 1.0), 8),
+        ((A, A, A, 4, 64, -1, 1.0), 8),
+        ((A + 1, A, A, 4, 64, 0, 1.0), 4),
+        ((A, A + 2, A, 4, 64, 1, 1.0), 4),
+        ((A, A, A + 2, 4, 64, 0, 1.0), 4),
+        ((A, A, A, 4, 64, 0, float("nan")), 5),
+        ((A, A, A, 4, 64, 1, float("inf")), 5),
+        ((A, A, A, 1 << 31, 64, 0, 1.0), 6),
+        ((A, A, A, 4, 1 << 31, 1, 1.0), 6),
+    ],
+)
+def test_softmax_validation_rejects_before_any_hip_call(lib, args, status):
+    got = lib.mifa_softmax_rows_raw(*args, None)
+    assert got == status, (args, got, lib.mifa_status_string(got))
+
+
+def test_softmax_validation_order(lib):
+    assert lib.mifa_softmax_rows_raw(0, A, A, 0, 0, 9, float("nan"), None) == 1
+    assert lib.mifa_softmax_rows_raw(A, A, A, 0, 1, 9, float("nan"), None) == 2
+    assert lib.mifa_softmax_rows_raw(A, A, A, 1, 1, 9, float("nan"), None) == 8
+    assert lib.mifa_softmax_rows_raw(A + 1, A, A, 1, 1, 0, float("nan"), None) == 4
+    # bf16 needs 2-byte alignment only; an odd address is rejected, an even one passes this check
+    assert lib.mifa_softmax_rows_raw(A + 2, A, A, 1, 1, 0, float("nan"), None) == 5
+    # a NULL lse is allowed (the check moves on to the scale)
+    assert lib.mifa_softmax_rows_raw(A, A, 0, 1, 1, 1, float("nan"), None) == 5
+
+
+def test_softmax_binding_python_checks(lib):
+    import torch
+
+    with pytest.raises(ValueError):
+        lib.softmax_rows(torch.zeros(2, 8))  # CPU tensors are rejected before any call

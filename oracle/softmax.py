@@ -45,7 +45,9 @@ def _widen(x) -> np.ndarray:
 # ---- the steps of the plain definition -----------------------------------------------------
 
 def _scaled(x: np.ndarray, c: float) -> np.ndarray:
-    return c * x
+    """c * x, with -inf entries kept at -inf (no weight) whatever the sign of c."""
+    with np.errstate(invalid="ignore"):
+        return np.where(np.isneginf(x), -np.inf, c * x)
 
 
 def _row_max(s: np.ndarray) -> np.ndarray:
@@ -94,7 +96,7 @@ def softmax_online_fp64(x, scale: float = 1.0, block: int = 16):
     y = np.empty_like(rows)
     lse = np.empty(rows.shape[0])
     for r in range(rows.shape[0]):
-        s = c * rows[r]
+        s = np.array([-np.inf if v == -np.inf else c * v for v in rows[r]])
         m, l = -np.inf, 0.0
         for j0 in range(0, C, block):
             blk = s[j0:j0 + block]

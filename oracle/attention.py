@@ -21,8 +21,11 @@ by V.  For each (b, h):
     LSE_i = m_i + log(sum_j exp(S_ij - m_i))   (natural log of the row's partition sum)
 
 Readings taken where the pages are silent: tensors are [B, H, N, d] with d fastest; the
-causal mask keeps key j for query i iff j <= i (square N); LSE uses the natural log of the
-scaled logits; the scale is used exactly as passed (callers pass the float32 value that the
+causal mask keeps key j for query i iff j <= i (square N); with fewer queries than keys
+(Nq < Nk, e.g. the newest Nq positions of a sequence whose keys are cached) the queries are
+the last Nq positions, so query i keeps key j iff j <= i + (Nk - Nq), which is the square
+mask restricted to those rows; Nq > Nk is not defined for the causal variant; LSE uses the
+natural log of the scaled logits; the scale is used exactly as passed (callers pass the float32 value that the
 GPU library receives).  Inputs may be bf16 values carried in any wider float type; they are
 widened exactly to float64.
 
@@ -68,7 +71,7 @@ def _scores(qh: np.ndarray, kh: np.ndarray, c: float) -> np.ndarray:
 
 
 def _causal_mask(s: np.ndarray, rows: np.ndarray) -> np.ndarray:
-    """Set S[r, j] = -inf where key j lies after query rows[r] (j > i)."""
+    """Set S[r, j] = -inf where key j lies after the position rows[r] of query r (j > pos)."""
     keys = np.arange(s.shape[1])
     out = s.copy()
     out[keys[None, :] > rows[:, None]] = -np.inf
@@ -109,20 +112,20 @@ def _head(qh, kh, vh, causal: bool, c: float, rows: np.ndarray):
 def attention_fp64(q, k, v, causal: bool = False, scale=None):
     """Exact attention in float64.
 
-    q: [B, H, Nq, d], k: [B, H, Nk, d], v: [B, H, Nk, dv].  Causal requires Nq == Nk.
-    Returns (O [B, H, Nq, dv] float64, LSE [B, H, Nq] float64)."""
+    q: [B, H, Nq, d], k: [B, H, Nk, d], v: [B, H, Nk, dv].  Causal requires Nq <= Nk; query i
+    sits at position i + Nk - Nq.  Returns (O [B, H, Nq, dv] float64, LSE [B, H, Nq] float64)."""
     q, k, v = _widen(q), _widen(k), _widen(v)
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be 4-D [B, H, N, d]")
     B, H, Nq, d = q.shape
     if k.shape[:2] != (B, H) or v.shape[:2] != (B, H) or k.shape[3] != d or k.shape[2] != v.shape[2]:
         raise ValueError("shape mismatch between q, k and v")
-    if causal and k.shape[2] != Nq:
-        raise ValueError("the causal variant is defined for square attention only")
+    if causal and k.shape[2] < Nq:
+        raise ValueError("the causal variant needs Nq <= Nk")
     c = _scale(d, scale)
     o = np.empty((B, H, Nq, v.shape[3]), dtype=np.float64)
     lse = np.empty((B, H, Nq), dtype=np.float64)
-    rows = np.arange(Nq)
+    rows = np.arange(Nq) + (k.shape[2] - Nq)
     for b in range(B):
         for h in range(H):
             o[b, h], lse[b, h] = _head(q[b, h], k[b, h], v[b, h], causal, c, rows)
@@ -138,6 +141,9 @@ def attention_fp64_rows(q, k, v, rows, causal: bool = False, scale=None):
     Returns (O [R, dv] float64, LSE [R] float64)."""
     rows = np.asarray(rows.cpu() if hasattr(rows, "cpu") else rows, dtype=np.int64)
     d = q.shape[3]
+    shift = k.shape[2] - q.shape[2]  # position of query i is i + Nk - Nq
+    if causal and shift < 0:
+        raise ValueError("the causal variant needs Nq <= Nk")
     c = _scale(d, scale)
     o = np.empty((rows.shape[0], v.shape[3]), dtype=np.float64)
     lse = np.empty(rows.shape[0], dtype=np.float64)
@@ -148,7 +154,7 @@ def attention_fp64_rows(q, k, v, rows, causal: bool = False, scale=None):
         kh, vh = _widen(k[b, h]), _widen(v[b, h])
         qi = rows[idx, 2]
         qh = _widen(q[b, h])[qi]
-        o[idx], lse[idx] = _head(qh, kh, vh, causal, c, qi)
+        o[idx], lse[idx] = _head(qh, kh, vh, causal, c, qi + shift)
     return o, lse
 
 
@@ -166,7 +172,7 @@ def attention_online_fp64(q, k, v, causal: bool = False, scale=None, block: int 
     c = _scale(d, scale)
     o = np.empty((B, H, N, v.shape[3]))
     lse = np.empty((B, H, N))
-    qi = np.arange(N)
+    qi = np.arange(N) + (Nk - N)  # query positions (bottom-right when N < Nk)
     for b in range(B):
         for h in range(H):
             m = np.full(N, -np.inf)

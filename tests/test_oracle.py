@@ -361,3 +361,63 @@ def test_accepts_bf16_torch_tensors():
     o, lse = OA.attention_fp64(q, k, v, causal=True, scale=0.5)
     o2, lse2 = OA.attention_fp64(q.double().numpy(), k.double().numpy(), v.double().numpy(), causal=True, scale=0.5)
     assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+# ---- fewer queries than keys (the newest Nq positions of a longer sequence) -------------------
+
+def test_rect_causal_is_the_square_mask_on_the_last_rows():
+    """Nq < Nk causal equals the last Nq rows of the square causal problem over all Nk
+    positions (queries are the newest positions): checked against the square definition."""
+    rng = _rng(31)
+    B, H, Nk, d = 1, 2, 23, 5
+    qf = _rand(rng, B, H, Nk, d)
+    k = _rand(rng, B, H, Nk, d)
+    v = _rand(rng, B, H, Nk, 3)
+    of, lf = OA.attention_fp64(qf, k, v, causal=True, scale=0.6)
+    for nq in (1, 2, 7, 23):
+        o, lse = OA.attention_fp64(qf[:, :, Nk - nq:], k, v, causal=True, scale=0.6)
+        np.testing.assert_allclose(o, of[:, :, Nk - nq:], atol=1e-13)
+        np.testing.assert_allclose(lse, lf[:, :, Nk - nq:], atol=1e-13)
+        rows = np.array([[0, h, i] for h in range(H) for i in range(nq)])
+        ro, rl = OA.attention_fp64_rows(qf[:, :, Nk - nq:], k, v, rows, causal=True, scale=0.6)
+        np.testing.assert_allclose(ro, o.reshape(-1, 3), atol=1e-13)
+        np.testing.assert_allclose(rl, lse.reshape(-1), atol=1e-13)
+        oo, lo = OA.attention_online_fp64(qf[:, :, Nk - nq:], k, v, causal=True, scale=0.6, block=4)
+        np.testing.assert_allclose(oo, o, atol=1e-12)
+        np.testing.assert_allclose(lo, lse, atol=1e-12)
+
+
+def test_rect_single_query_causal_sees_every_key():
+    rng = _rng(32)
+    q = _rand(rng, 2, 3, 1, 8)
+    k = _rand(rng, 2, 3, 40, 8)
+    v = _rand(rng, 2, 3, 40, 8)
+    oc, lc = OA.attention_fp64(q, k, v, causal=True, scale=0.3)
+    on, ln_ = OA.attention_fp64(q, k, v, causal=False, scale=0.3)
+    np.testing.assert_allclose(oc, on, atol=1e-15)
+    np.testing.assert_allclose(lc, ln_, atol=1e-15)
+
+
+def test_rect_causal_brute_force():
+    """Pure-Python loops: query i (of Nq) at position i + Nk - Nq sees keys j <= that position."""
+    rng = _rng(33)
+    Nq, Nk, d, dv = 3, 7, 4, 2
+    q, k, v = _rand(rng, 1, 1, Nq, d), _rand(rng, 1, 1, Nk, d), _rand(rng, 1, 1, Nk, dv)
+    o, lse = OA.attention_fp64(q, k, v, causal=True, scale=0.9)
+    for i in range(Nq):
+        pos = i + Nk - Nq
+        w = [math.exp(0.9 * sum(float(q[0, 0, i, t]) * float(k[0, 0, j, t]) for t in range(d))) for j in range(pos + 1)]
+        z = sum(w)
+        for c in range(dv):
+            ref = sum(w[j] * float(v[0, 0, j, c]) for j in range(pos + 1)) / z
+            assert abs(o[0, 0, i, c] - ref) <= 1e-12
+        assert abs(lse[0, 0, i] - math.log(z)) <= 1e-12
+
+
+def test_rect_causal_more_queries_than_keys_is_rejected():
+    rng = _rng(34)
+    q, k = _rand(rng, 1, 1, 5, 4), _rand(rng, 1, 1, 4, 4)
+    with pytest.raises(ValueError):
+        OA.attention_fp64(q, k, k, causal=True)
+    with pytest.raises(ValueError):
+        OA.attention_fp64_rows(q, k, k, np.array([[0, 0, 0]]), causal=True)

@@ -10,7 +10,11 @@ the timed region.  Prints ONE JSON line on stdout.
 
 FLOPs per step follow the usual attention convention: 4*B*H*N^2*d, halved for causal.
 
-`--workload SM1` .. `SM4` time the stand-alone row softmax (mifa_softmax_rows) instead: one
+`--workload D1` / `D2` time the split-KV path (mifa_attention_splitkv) on few queries against a
+long key/value cache; the metric is HBM throughput of the compulsory bytes (Q, K, V read once,
+O and LSE written once).
+
+`--workload SM1` .. `SM5` time the stand-alone row softmax (mifa_softmax_rows) instead: one
 step is one launch over a [rows, cols] matrix, and the metric is HBM throughput of the
 compulsory bytes (the input read once, the output and the row LSE written once).
 """
@@ -154,6 +158,117 @@ def softmax_cpu_baseline(w, x, rows_count: int):
     }
 
 
+def decode_bytes(w) -> int:
+    """Compulsory bytes of one split-KV launch: bf16 Q, K, V read once, fp32 O and LSE written."""
+    return 2 * w.B * w.H * (w.Nq + 2 * w.Nk) * w.d + 4 * w.B * w.H * w.Nq * (w.d + 1)
+
+
+def decode_flops(w) -> float:
+    """4 d FLOPs per (query, visible key) pair."""
+    if not w.causal:
+        pairs = w.Nq * w.Nk
+    else:
+        pairs = sum(w.Nk - w.Nq + 1 + i for i in range(w.Nq))
+    return 4.0 * w.B * w.H * pairs * w.d
+
+
+def bench_decode(args):
+    import torch
+
+    from io_aware_softmax_mifa_amd import binding
+    from io_aware_softmax_mifa_amd import workloads as W
+
+    w = W.decode_by_name(args.workload)
+    log(f"workload {w.name}: B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} d={w.d} causal={w.causal}")
+    q, k, v = W.make_rect_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.seed, w.dist)
+    scale = W.fp32_scale(w.d)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dq, dk, dv = (t.to(dev) for t in (q, k, v))
+    o = torch.empty((w.B, w.H, w.Nq, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    need = binding.mifa_splitkv_workspace_bytes(w.B, w.H, w.Nq, w.Nk, w.d)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        st = binding.mifa_attention_splitkv_raw(dq, dk, dv, o, lse, w.B, w.H, w.Nq, w.Nk, w.d, w.causal, scale, ws,
+                                                ws.numel(), stream.cuda_stream)
+        if st != 0:
+            raise binding.MifaError(st, binding.mifa_status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    call_ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / args.steps
+    if args.copy_calibration:
+        copy_calibration(dev)
+    nbytes = decode_bytes(w)
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {call_ms:.4f} ms/call (HIP events; both kernels)")
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    out = {
+        "metric": "attention decode (split-KV) HBM throughput (compulsory bytes) and % of MI355X HBM bandwidth",
+        "value": nbytes / (ms_per_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. bf16 Q/K/V)",
+        "config": {
+            "workload": f"{w.name}: B={w.B} H={w.H} Nq={w.Nq} Nk={w.Nk} d={w.d} causal={int(w.causal)} bf16 "
+                        f"Q,K,V ~ N(0,1); fp32 O + LSE; split-KV + merge",
+            "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": bool(w.causal),
+            "compulsory_hbm_bytes": nbytes,
+            "flop_per_step": decode_flops(w),
+            "call_ms": call_ms,
+            "workspace_bytes": need,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS,
+            "traffic": measured_traffic(w.name, KERNEL_SOURCE),
+        },
+    }
+    if args.no_cpu_baseline:
+        out["cpu_baseline"] = None
+    else:
+        from oracle import attention_fp64_rows
+
+        rows = torch.tensor([[b, h, i] for b in range(w.B) for h in range(w.H) for i in range(w.Nq)])
+        t0 = time.perf_counter()
+        attention_fp64_rows(q, k, v, rows, causal=w.causal, scale=scale)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": nbytes / dt / 1e9,
+            "unit": "GB/s",
+            "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"every one of the {rows.shape[0]} query rows (float64 NumPy oracle), {dt:.2f} s",
+            "seconds": dt,
+            "host_cpus": os.cpu_count(),
+        }
+    print(json.dumps(out), flush=True)
+
+
 def bench_softmax(args):
     import torch
 
@@ -248,6 +363,8 @@ def main():
 
     if args.workload.startswith("SM"):
         return bench_softmax(args)
+    if args.workload.startswith("D"):
+        return bench_decode(args)
 
     import torch
 

@@ -40,13 +40,14 @@ extern "C" {
 typedef enum mifa_status {
   MIFA_OK = 0,
   MIFA_ERR_NULL_POINTER = 1,   /* q, k, v, o or lse is NULL */
-  MIFA_ERR_BAD_SHAPE = 2,      /* B, H or N < 1 */
+  MIFA_ERR_BAD_SHAPE = 2,      /* B, H or N (Nq, Nk) < 1, or causal with Nq > Nk */
   MIFA_ERR_UNSUPPORTED_D = 3,  /* head dimension d is not 64 or 128 */
   MIFA_ERR_MISALIGNED = 4,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   MIFA_ERR_BAD_SCALE = 5,      /* scale is NaN or infinite */
   MIFA_ERR_TOO_LARGE = 6,      /* N*d >= 2^31, or B*H*ceil(N/128) >= 2^31 work tiles */
   MIFA_ERR_HIP = 7,            /* the HIP runtime rejected the launch; see mifa_last_hip_error */
-  MIFA_ERR_BAD_DTYPE = 8       /* dtype is not one of mifa_dtype (mifa_softmax_rows) */
+  MIFA_ERR_BAD_DTYPE = 8,      /* dtype is not one of mifa_dtype (mifa_softmax_rows) */
+  MIFA_ERR_WORKSPACE = 9       /* workspace NULL, misaligned or too small (mifa_attention_splitkv) */
 } mifa_status;
 
 /* Element types of mifa_softmax_rows. */
@@ -78,6 +79,46 @@ typedef enum mifa_dtype {
 int mifa_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
              int64_t B, int64_t H, int64_t N, int64_t d, int causal, float scale,
              void* stream);
+
+/*
+ * mifa_attention -- the same operation with Nq queries and Nk keys per head (Nq != Nk allowed).
+ *
+ *   q        bf16 [B, H, Nq, d]; k, v bf16 [B, H, Nk, d]; o float32 [B, H, Nq, d];
+ *            lse float32 [B, H, Nq].  Layout, alignment and ownership as for mifa_fwd.
+ *   causal   Non-zero: the queries are the last Nq positions of the Nk-long sequence, so query
+ *            i sees keys j <= i + (Nk - Nq) -- the lower-triangular mask of the square case
+ *            (the causal remark in the Hacker News FlashAttention-3 thread) restricted to
+ *            those rows.  Requires Nq <= Nk (MIFA_ERR_BAD_SHAPE otherwise).
+ * mifa_fwd(..., N, ...) is mifa_attention(..., N, N, ...).  Errors as for mifa_fwd.
+ */
+int mifa_attention(const void* q, const void* k, const void* v, float* o, float* lse,
+                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
+                   void* stream);
+
+/*
+ * mifa_attention_splitkv -- mifa_attention with the keys of each head cut into ranges that
+ * separate workgroups process in parallel, for few queries against many keys (decoding with a
+ * key/value cache).  Each range produces the attention over its keys alone, a partial O and
+ * its LSE; a second kernel merges the ranges with the associative rule
+ *     LSE = ln sum_s exp(LSE_s),  O = sum_s exp(LSE_s - LSE) O_s
+ * (the partial softmax states combine as aggregates, as the Hacker News FlashAttention-3 thread
+ * puts it; the same rescaling as the online softmax).  The result equals mifa_attention's up
+ * to fp32 rounding order.
+ *
+ *   workspace        device memory the caller owns, 16-byte aligned, at least
+ *                    mifa_splitkv_workspace_bytes(B, H, Nq, Nk, d) bytes; overwritten (it holds
+ *                    the partial O and LSE); the caller must not touch it until the stream has
+ *                    passed the call.  Calls that share a workspace must be ordered on a stream.
+ *   workspace_bytes  its size in bytes.
+ * Other arguments and errors as for mifa_attention, plus MIFA_ERR_WORKSPACE (checked after the
+ * other arguments).  When one range suffices the workspace is not used.
+ */
+int mifa_attention_splitkv(const void* q, const void* k, const void* v, float* o, float* lse,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                           float scale, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes mifa_attention_splitkv needs for this shape (0 for an invalid shape). */
+int64_t mifa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d);
 
 /*
  * mifa_softmax_rows -- the row softmax on its own, with the online normaliser.

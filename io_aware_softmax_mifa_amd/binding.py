@@ -26,9 +26,11 @@ STATUS_NAMES = {
     6: "MIFA_ERR_TOO_LARGE",
     7: "MIFA_ERR_HIP",
     8: "MIFA_ERR_BAD_DTYPE",
+    9: "MIFA_ERR_WORKSPACE",
 }
 MIFA_DTYPE_BF16, MIFA_DTYPE_F32 = 0, 1
-EXPORTED = ("mifa_fwd", "mifa_softmax_rows", "mifa_status_string", "mifa_version", "mifa_last_hip_error")
+EXPORTED = ("mifa_fwd", "mifa_attention", "mifa_attention_splitkv", "mifa_splitkv_workspace_bytes",
+            "mifa_softmax_rows", "mifa_status_string", "mifa_version", "mifa_last_hip_error")
 
 
 class MifaError(RuntimeError):
@@ -46,6 +48,15 @@ def _load() -> ctypes.CDLL:
     lib.mifa_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_float,
                                                                              ctypes.c_void_p]
     lib.mifa_fwd.restype = ctypes.c_int
+    lib.mifa_attention.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [ctypes.c_int, ctypes.c_float,
+                                                                                   ctypes.c_void_p]
+    lib.mifa_attention.restype = ctypes.c_int
+    lib.mifa_attention_splitkv.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 +
+                                           [ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64,
+                                            ctypes.c_void_p])
+    lib.mifa_attention_splitkv.restype = ctypes.c_int
+    lib.mifa_splitkv_workspace_bytes.argtypes = [ctypes.c_int64] * 5
+    lib.mifa_splitkv_workspace_bytes.restype = ctypes.c_int64
     lib.mifa_softmax_rows.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_float,
                                                                                       ctypes.c_void_p]
     lib.mifa_softmax_rows.restype = ctypes.c_int
@@ -101,6 +112,28 @@ def mifa_fwd(q, k, v, o, lse, B, H, N, d, causal, scale, stream=None) -> None:
         raise MifaError(st, mifa_status_string(st) + extra)
 
 
+def _raise(st):
+    if st != MIFA_OK:
+        extra = f" (hipError {mifa_last_hip_error()})" if st == 7 else ""
+        raise MifaError(st, mifa_status_string(st) + extra)
+
+
+def mifa_attention_raw(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream) -> int:
+    return int(_lib.mifa_attention(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq), int(Nk),
+                                   int(d), 1 if causal else 0, float(scale), stream or None))
+
+
+def mifa_attention_splitkv_raw(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, workspace, workspace_bytes,
+                               stream) -> int:
+    return int(_lib.mifa_attention_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq),
+                                           int(Nk), int(d), 1 if causal else 0, float(scale), _ptr(workspace),
+                                           int(workspace_bytes), stream or None))
+
+
+def mifa_splitkv_workspace_bytes(B, H, Nq, Nk, d) -> int:
+    return int(_lib.mifa_splitkv_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(d)))
+
+
 def _check(name, t, shape=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -116,31 +149,69 @@ def _check(name, t, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
 
 
-def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale=None,
-              out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    """Exact attention forward.  q, k, v: bf16 [B, H, N, d] on the GPU (d = 64 or 128).
-
-    Returns (O float32 [B, H, N, d], LSE float32 [B, H, N]); both are allocated here unless
-    given.  The launch is asynchronous on torch's current stream."""
-    _check("q", q)
-    shape = tuple(q.shape)
-    _check("k", k, shape)
-    _check("v", v, shape)
-    if not (q.device == k.device == v.device):
-        raise ValueError("q, k, v must be on one device")
-    B, H, N, d = shape
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
+def _outputs(q, out, lse):
+    B, H, Nq, d = q.shape
     if out is None:
-        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+        out = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
     if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
     if out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous() or out.device != q.device:
         raise ValueError("out must be a contiguous float32 tensor shaped like q on q's device")
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
+    return out, lse
+
+
+def _qkv(q, k, v):
+    _check("q", q)
+    _check("k", k)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape != (B, H, Nk, d):
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected {(B, H, Nk, d)}")
+    _check("v", v, (B, H, Nk, d))
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one device")
+    return B, H, Nq, Nk, d
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale=None,
+              out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Exact attention forward.  q: bf16 [B, H, Nq, d], k, v: bf16 [B, H, Nk, d] on the GPU
+    (d = 64 or 128; causal needs Nq <= Nk, the queries being the last Nq positions).
+
+    Returns (O float32 [B, H, Nq, d], LSE float32 [B, H, Nq]); both are allocated here unless
+    given.  The launch is asynchronous on torch's current stream."""
+    B, H, Nq, Nk, d = _qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse)
     with torch.cuda.device(q.device):
-        mifa_fwd(q, k, v, out, lse, B, H, N, d, causal, scale, torch.cuda.current_stream(q.device).cuda_stream)
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        if Nq == Nk:
+            mifa_fwd(q, k, v, out, lse, B, H, Nq, d, causal, scale, stream)
+        else:
+            _raise(mifa_attention_raw(q, k, v, out, lse, B, H, Nq, Nk, d, causal, scale, stream))
+    return out, lse
+
+
+def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale=None,
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None):
+    """attention() with each head's keys split into ranges processed in parallel and merged
+    by LSE (for few queries against many keys).  `workspace`: a GPU tensor of at least
+    mifa_splitkv_workspace_bytes(...) bytes, allocated here (uint8) unless given."""
+    B, H, Nq, Nk, d = _qkv(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out, lse = _outputs(q, out, lse)
+    need = mifa_splitkv_workspace_bytes(B, H, Nq, Nk, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        _raise(mifa_attention_splitkv_raw(q, k, v, out, lse, B, H, Nq, Nk, d, causal, scale, workspace, nbytes,
+                                          torch.cuda.current_stream(q.device).cuda_stream))
     return out, lse
 
 

@@ -278,7 +278,9 @@ struct Wave {
   float m_run;  // running max in log2 units (stale by at most kRescaleSlack)
   float l_run;  // this lane's half of the row sum
   float c;      // |scale| * log2(e), >= 1e-30
-  int N, row0, my_row, hf;
+  int N;       // keys from this workgroup's first key block to the end of the sequence
+  int row0, my_row, hf;
+  int my_pos;  // causal: this row's last visible key, counted from the first key block
   Lane<C> la;
 
   // ---- S^T = K Q^T for one block: step i is d slice i / kKT of key tile i % kKT ----
@@ -316,7 +318,7 @@ struct Wave {
   __device__ __forceinline__ void apply_mask(f32x16 (&sacc)[C::kKT], int key0) {
     // Key offset 32kt + 8(i/4) + (i%4) within the block is visible iff it is <= lim.
     int lim = N - 1 - key0 - 4 * hf;
-    if (CAUSAL) lim = min(lim, my_row - key0 - 4 * hf);
+    if (CAUSAL) lim = min(lim, my_pos - key0 - 4 * hf);
 #pragma unroll
     for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
@@ -356,7 +358,10 @@ struct Wave {
   // A masked score is -inf and c > 0, so its weight is exp2(-inf) = 0.
   __device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[C::kKT], bf16x8 (&pb)[C::kKS]) {
     float ls4[4];
-    const float neg_m = -m_run;
+    // A row that has seen no visible key yet (m = -inf; possible when the workgroup covers a
+    // key range that starts after the row's last key) must get weight exp2(-inf) = 0, not
+    // exp2(-inf + inf).
+    const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
 #pragma unroll
     for (int kt = 0; kt < C::kKT; ++kt)
 #pragma unroll
@@ -440,13 +445,31 @@ struct Wave {
   }
 };
 
+// Launch parameters.  Nq query rows and Nk keys per head; query i sits at position
+// i + Nk - Nq (so with Nq < Nk the queries are the newest positions, and the causal mask keeps
+// key j iff j <= i + Nk - Nq).  With n_splits > 1 the keys are cut into ranges of split_blocks
+// key blocks and split s writes the attention over its range alone (O normalised over that
+// range, LSE of that range; O = 0 and LSE = -inf where the range holds no visible key) to
+// o + s o_split and lse + s lse_split.
+struct FwdParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  float* o;
+  float* lse;
+  int Nq, Nk, BH, n_qtiles;
+  float c_log2;
+  int negate_q, xcd_group;
+  int n_splits, split_blocks;
+  int64_t o_split, lse_split;
+};
+
 template <typename C, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(C::kThreads, C::kThreads), amdgpu_waves_per_eu(2, 2)))
-void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
-                     const __bf16* __restrict__ v, float* __restrict__ o, float* __restrict__ lse,
-                     int N, int BH, int n_qtiles, float c_log2, int negate_q, int xcd_group) {
+void mifa_fwd_kernel(FwdParams p) {
   constexpr int D = C::D, BC = C::BC, NBUF = C::NBUF, kBR = C::kBR;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int BH = p.BH, n_qtiles = p.n_qtiles;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -454,11 +477,13 @@ void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   const int ln = lane & 31;
   const int hf = lane >> 5;
 
-  // ---- which (b*H + h, q-tile) this workgroup owns ----
+  // ---- which (key range, b*H + h, q-tile) this workgroup owns ----
+  const int tiles = BH * n_qtiles;
+  const int split = blockIdx.x / tiles;
   int bh, qt;
   {
-    const int w = blockIdx.x;
-    if (xcd_group) {
+    const int w = blockIdx.x - split * tiles;
+    if (p.xcd_group) {
       // Workgroup w runs on XCD w % 8; give XCD x the heads bh = x, x + 8, ... and walk them
       // heaviest tile first.
       const int x = w % kXcds, kk = w / kXcds;
@@ -472,17 +497,39 @@ void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
       qt = CAUSAL ? n_qtiles - 1 - rank : rank;
     }
   }
-  const int64_t head_off = (int64_t)bh * N * D;
-  const __bf16* __restrict__ qh = q + head_off;
-  const __bf16* __restrict__ kh = k + head_off;
-  const __bf16* __restrict__ vh = v + head_off;
+  const int Nq = p.Nq, Nk = p.Nk, kshift = Nk - Nq;
+
+  // Blocks [jb0, jb1) of the head's keys are visited: the tile's visible blocks, cut to this
+  // workgroup's key range.  Blocks from j_mask on straddle the diagonal or the end of the
+  // sequence and take the masked path.
+  const int n_kblocks = (Nk + BC - 1) / BC;
+  int nblk_all = n_kblocks;
+  int j_mask_all = Nk / BC;
+  if (CAUSAL) {
+    const int last_row = min(Nq - 1, qt * kBR + kBR - 1);
+    nblk_all = min(n_kblocks, (last_row + kshift) / BC + 1);
+    j_mask_all = min(j_mask_all, (qt * kBR + kshift) / BC);
+  }
+  const int jb0 = split * p.split_blocks;
+  const int jb1 = min(nblk_all, jb0 + p.split_blocks);
+  const int nblk = jb1 - jb0;
+  const int j_mask = j_mask_all - jb0;
+  const int key_base = jb0 * BC;
+
+  const __bf16* __restrict__ qh = p.q + (int64_t)bh * Nq * D;
+  const __bf16* __restrict__ kh = p.k + ((int64_t)bh * Nk + key_base) * D;
+  const __bf16* __restrict__ vh = p.v + ((int64_t)bh * Nk + key_base) * D;
+  float* __restrict__ o_out = p.o + split * p.o_split + (int64_t)bh * Nq * D;
+  float* __restrict__ lse_out = p.lse + split * p.lse_split + (int64_t)bh * Nq;
 
   Wave<C, CAUSAL> W;
+  const int N = Nk - key_base;
   W.N = N;
   W.row0 = qt * kBR + wave * kRowsPerWave;
   W.my_row = W.row0 + ln;
+  W.my_pos = W.my_row + kshift - key_base;
   W.hf = hf;
-  W.c = c_log2;
+  W.c = p.c_log2;
   W.m_run = -__builtin_inff();
   W.l_run = 0.f;
 #pragma unroll
@@ -490,25 +537,27 @@ void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
 
   // ---- Q rows into VGPRs (B operand of S^T = K Q^T: lane holds q[row][16s + 8hf .. +7]) ----
   {
-    const int r = W.my_row < N ? W.my_row : N - 1;
+    const int r = W.my_row < Nq ? W.my_row : Nq - 1;
     const __bf16* src = qh + (int64_t)r * D + 8 * hf;
 #pragma unroll
     for (int s = 0; s < C::kDS; ++s) {
       u32x4 raw = *(const u32x4*)(src + 16 * s);
-      if (negate_q) raw ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      if (p.negate_q) raw ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
       W.qf[s] = __builtin_bit_cast(bf16x8, raw);
     }
   }
 
-  // Blocks [0, nblk) are visited; blocks [j_mask, nblk) straddle the diagonal or the end of the
-  // sequence and take the masked path.
-  const int n_kblocks = (N + BC - 1) / BC;
-  int nblk = n_kblocks;
-  int j_mask = N / BC;
-  if (CAUSAL) {
-    const int last_row = min(N - 1, qt * kBR + kBR - 1);
-    nblk = last_row / BC + 1;
-    j_mask = min(j_mask, (qt * kBR) / BC);
+  // A key range that holds no block of this tile (a split past the causal diagonal) still
+  // writes its part: no weight (O = 0, LSE = -inf).  The test is uniform over the workgroup.
+  if (nblk <= 0) {
+    if (W.my_row < Nq) {
+#pragma unroll
+      for (int t = 0; t < C::kDT; ++t)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) *(f32x4*)(o_out + (int64_t)W.my_row * D + 32 * t + 8 * g4 + 4 * hf) = (f32x4){};
+      if (hf == 0) lse_out[W.my_row] = -__builtin_inff();
+    }
+    return;
   }
 
   const unsigned smem_base = (unsigned)(uintptr_t)(lds_void*)smem;
@@ -589,10 +638,11 @@ void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
   wait_vmcnt<0>();
 
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ----
+  // (A row with no visible key in this workgroup's key range has l = 0: O = 0, LSE = -inf.)
   const float l_tot = half_sum(W.l_run);
-  if (W.my_row < N) {
-    const float inv = 1.f / l_tot;
-    float* orow = o + head_off + (int64_t)W.my_row * D;
+  if (W.my_row < Nq) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    float* orow = o_out + (int64_t)W.my_row * D;
 #pragma unroll
     for (int t = 0; t < C::kDT; ++t)
 #pragma unroll
@@ -601,47 +651,135 @@ void mifa_fwd_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                      W.oacc[t][4 * g4 + 3] * inv};
         *(f32x4*)(orow + 32 * t + 8 * g4 + 4 * hf) = val;
       }
-    if (hf == 0) lse[(int64_t)bh * N + W.my_row] = (W.m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
+    if (hf == 0) lse_out[W.my_row] = (W.m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
   }
 }
 
+// Shape of one launch on the host side.
+struct Problem {
+  const void *q, *k, *v;
+  float *o, *lse;
+  int Nq, Nk, BH;
+  float scale;
+  int n_splits, split_blocks;
+  int64_t o_split, lse_split;
+};
+
 template <typename C, bool CAUSAL>
-hipError_t launch(const void* q, const void* k, const void* v, float* o, float* lse, int N, int BH,
-                  float scale, hipStream_t stream) {
-  const int n_qtiles = (N + C::kBR - 1) / C::kBR;
-  const int64_t tiles = (int64_t)BH * n_qtiles;
-  const int xcd_group = (BH % kXcds == 0) ? 1 : 0;
-  const int negate_q = scale < 0.f ? 1 : 0;
+hipError_t launch(const Problem& pr, hipStream_t stream) {
+  FwdParams p;
+  p.q = (const __bf16*)pr.q;
+  p.k = (const __bf16*)pr.k;
+  p.v = (const __bf16*)pr.v;
+  p.o = pr.o;
+  p.lse = pr.lse;
+  p.Nq = pr.Nq;
+  p.Nk = pr.Nk;
+  p.BH = pr.BH;
+  p.n_qtiles = (pr.Nq + C::kBR - 1) / C::kBR;
+  p.xcd_group = (pr.BH % kXcds == 0) ? 1 : 0;
+  p.negate_q = pr.scale < 0.f ? 1 : 0;
   // The exponent factor c = |scale| * log2(e) is kept >= 1e-30 so that a masked score (-inf)
   // always maps to exp2(-inf) = 0.  For |scale| below that every logit is under 1e-29 in
   // magnitude and exp2 of it rounds to exactly 1 in fp32, the same as with scale = 0.
-  double c_exact = (double)(negate_q ? -scale : scale) * 1.4426950408889634;
+  double c_exact = (double)(p.negate_q ? -pr.scale : pr.scale) * 1.4426950408889634;
   if (c_exact < 1e-30) c_exact = 1e-30;
-  const float c_log2 = (float)c_exact;
+  p.c_log2 = (float)c_exact;
+  p.n_splits = pr.n_splits;
+  p.split_blocks = pr.split_blocks;
+  p.o_split = pr.o_split;
+  p.lse_split = pr.lse_split;
+  const int64_t grid = (int64_t)pr.BH * p.n_qtiles * pr.n_splits;
   auto kern = mifa_fwd_kernel<C, CAUSAL>;
   // Raise the dynamic-LDS limit once per instantiation (thread-safe static initialisation).
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(C::kThreads), C::kLdsBytes, stream,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, o, lse, N, BH, n_qtiles, c_log2,
-                     negate_q, xcd_group);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, stream, p);
   return hipGetLastError();
 }
 
 // Launch-shape choice: 8-wave workgroups (256 rows, one per CU) for long sequences with at least
 // as many of them as CUs; otherwise 4-wave workgroups (128 rows, two per CU).  Measured on
 // MI355X: B=1 H=32 N=16384 causal runs ~5 % faster with 8 waves, B=8 H=16 N=2048 causal ~9 %
-// faster with 4 (shorter tiles, better balance); N=4096 is about even.
+// faster with 4 (shorter tiles, better balance); N=4096 is about even.  Key-range splits always
+// use 4-wave workgroups.
 constexpr int kCUs = 256;
 constexpr int kLongN = 4096;
 template <int D, bool CAUSAL>
-hipError_t dispatch(const void* q, const void* k, const void* v, float* o, float* lse, int N, int BH,
-                    float scale, hipStream_t stream) {
-  const int64_t big_tiles = (int64_t)BH * ((N + 255) / 256);
-  if (N > kLongN && big_tiles >= kCUs)
-    return launch<Cfg<D, 64, 8, 4>, CAUSAL>(q, k, v, o, lse, N, BH, scale, stream);
-  return launch<Cfg<D, 64, 4, 2>, CAUSAL>(q, k, v, o, lse, N, BH, scale, stream);
+hipError_t dispatch(const Problem& pr, hipStream_t stream) {
+  const int64_t big_tiles = (int64_t)pr.BH * ((pr.Nq + 255) / 256);
+  if (pr.n_splits == 1 && pr.Nq > kLongN && big_tiles >= kCUs) return launch<Cfg<D, 64, 8, 4>, CAUSAL>(pr, stream);
+  return launch<Cfg<D, 64, 4, 2>, CAUSAL>(pr, stream);
+}
+
+hipError_t dispatch_d(const Problem& pr, int d, bool causal, hipStream_t s) {
+  if (d == 128) return causal ? dispatch<128, true>(pr, s) : dispatch<128, false>(pr, s);
+  return causal ? dispatch<64, true>(pr, s) : dispatch<64, false>(pr, s);
+}
+
+// ---- merge of key-range partials: the associative rule on (O_s, LSE_s) ----------------------
+// O = sum_s w_s O_s / sum_s w_s and LSE = m + ln sum_s w_s, with w_s = exp(LSE_s - m) and
+// m = max_s LSE_s.  One row per D/4 threads (four O elements each).
+template <int D>
+__global__ __launch_bounds__(256) void merge_splits(const float* __restrict__ o_part, const float* __restrict__ lse_part,
+                                                    float* __restrict__ o, float* __restrict__ lse, int64_t rows,
+                                                    int n_splits, int64_t o_split, int64_t lse_split) {
+  constexpr int TPR = D / 4, RPB = 256 / TPR;
+  const int t = threadIdx.x % TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (row >= rows) return;
+  float m = -__builtin_inff();
+  for (int s = 0; s < n_splits; ++s) m = __builtin_elementwise_maximum(m, lse_part[s * lse_split + row]);
+  f32x4 acc = {};
+  float wsum = 0.f;
+  for (int s = 0; s < n_splits; ++s) {
+    const float ls = lse_part[s * lse_split + row];
+    const float w = ls == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((ls - m) * 1.4426950408889634f);
+    wsum += w;
+    acc += w * *(const f32x4*)(o_part + s * o_split + row * D + 4 * t);
+  }
+  *(f32x4*)(o + row * D + 4 * t) = acc * (1.f / wsum);
+  if (t == 0) lse[row] = m + __builtin_amdgcn_logf(wsum) * 0.69314718055994531f;
+}
+
+// Key-range split for the split-KV entry point: enough workgroups to fill the machine twice
+// over (two 4-wave workgroups per CU), each range at least four key blocks long.
+struct Split {
+  int n_splits, split_blocks;
+};
+Split choose_split(int64_t BH, int64_t Nq, int64_t Nk) {
+  const int64_t tiles = BH * ((Nq + 127) / 128);
+  const int64_t kblocks = (Nk + 63) / 64;
+  int64_t want = (4 * kCUs + tiles - 1) / tiles;
+  want = want < 1 ? 1 : want;
+  int64_t most = (kblocks + 3) / 4;
+  most = most < 1 ? 1 : most;
+  const int64_t n = want < most ? want : most;
+  const int64_t per = (kblocks + n - 1) / n;
+  return Split{(int)((kblocks + per - 1) / per), (int)per};
+}
+
+int64_t workspace_bytes(int64_t BH, int64_t Nq, int64_t d, int n_splits) {
+  return (int64_t)n_splits * BH * Nq * (d + 1) * 4;
+}
+
+// Argument checks shared by the attention entry points, in the documented order.
+int check_attention(const void* q, const void* k, const void* v, const float* o, const float* lse, int64_t B,
+                    int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal, float scale) {
+  if (!q || !k || !v || !o || !lse) return MIFA_ERR_NULL_POINTER;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (causal && Nq > Nk)) return MIFA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return MIFA_ERR_UNSUPPORTED_D;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return MIFA_ERR_MISALIGNED;
+  if ((uintptr_t)lse & 3u) return MIFA_ERR_MISALIGNED;
+  if (!__builtin_isfinite(scale)) return MIFA_ERR_BAD_SCALE;
+  // Per-head offsets inside the kernel are 32-bit (N*d), the grid is 1-D (B*H*tiles*splits).
+  if (Nq * d >= ((int64_t)1 << 31) || Nk * d >= ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
+  if (B > ((int64_t)1 << 31) || H > ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
+  const int64_t BH = B * H;
+  const int64_t tiles = BH * ((Nq + 127) / 128);
+  if (BH >= ((int64_t)1 << 31) || tiles >= ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
+  return MIFA_OK;
 }
 
 thread_local int g_last_hip_error = 0;
@@ -650,29 +788,65 @@ thread_local int g_last_hip_error = 0;
 
 extern "C" {
 
+int mifa_attention(const void* q, const void* k, const void* v, float* o, float* lse, int64_t B, int64_t H,
+                   int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, void* stream) {
+  const int st = check_attention(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale);
+  if (st != MIFA_OK) return st;
+  const Problem pr{q, k, v, o, lse, (int)Nq, (int)Nk, (int)(B * H), scale, 1, 1 << 30, 0, 0};
+  const hipError_t e = dispatch_d(pr, (int)d, causal != 0, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return MIFA_ERR_HIP;
+  }
+  return MIFA_OK;
+}
+
 int mifa_fwd(const void* q, const void* k, const void* v, float* o, float* lse, int64_t B, int64_t H,
              int64_t N, int64_t d, int causal, float scale, void* stream) {
-  if (!q || !k || !v || !o || !lse) return MIFA_ERR_NULL_POINTER;
-  if (B < 1 || H < 1 || N < 1) return MIFA_ERR_BAD_SHAPE;
-  if (d != 64 && d != 128) return MIFA_ERR_UNSUPPORTED_D;
-  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return MIFA_ERR_MISALIGNED;
-  if ((uintptr_t)lse & 3u) return MIFA_ERR_MISALIGNED;
-  if (!__builtin_isfinite(scale)) return MIFA_ERR_BAD_SCALE;
-  // Per-head offsets inside the kernel are 32-bit (N*d), the grid is 1-D (B*H*tiles).
-  if (N * d >= ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
-  if (B > ((int64_t)1 << 31) || H > ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
-  const int64_t BH = B * H;
-  const int64_t tiles = BH * ((N + 127) / 128);
-  if (BH >= ((int64_t)1 << 31) || tiles >= ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
+  return mifa_attention(q, k, v, o, lse, B, H, N, N, d, causal, scale, stream);
+}
 
+int64_t mifa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d) {
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (d != 64 && d != 128)) return 0;
+  if (B > ((int64_t)1 << 31) || H > ((int64_t)1 << 31) || Nq >= ((int64_t)1 << 31) || Nk >= ((int64_t)1 << 31)) return 0;
+  const Split sp = choose_split(B * H, Nq, Nk);
+  return workspace_bytes(B * H, Nq, d, sp.n_splits);
+}
+
+int mifa_attention_splitkv(const void* q, const void* k, const void* v, float* o, float* lse, int64_t B, int64_t H,
+                           int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, void* workspace,
+                           int64_t workspace_bytes_given, void* stream) {
+  const int st = check_attention(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale);
+  if (st != MIFA_OK) return st;
+  const int64_t BH = B * H;
+  const Split sp = choose_split(BH, Nq, Nk);
+  if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes_given < workspace_bytes(BH, Nq, d, sp.n_splits))
+    return MIFA_ERR_WORKSPACE;
+  if (BH * ((Nq + 127) / 128) * sp.n_splits >= ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (d == 128)
-    e = causal ? dispatch<128, true>(q, k, v, o, lse, (int)N, (int)BH, scale, s)
-               : dispatch<128, false>(q, k, v, o, lse, (int)N, (int)BH, scale, s);
-  else
-    e = causal ? dispatch<64, true>(q, k, v, o, lse, (int)N, (int)BH, scale, s)
-               : dispatch<64, false>(q, k, v, o, lse, (int)N, (int)BH, scale, s);
+  if (sp.n_splits == 1) {
+    const Problem pr{q, k, v, o, lse, (int)Nq, (int)Nk, (int)BH, scale, 1, sp.split_blocks, 0, 0};
+    e = dispatch_d(pr, (int)d, causal != 0, s);
+  } else {
+    float* o_part = (float*)workspace;
+    float* lse_part = o_part + (int64_t)sp.n_splits * BH * Nq * d;
+    const Problem pr{q, k, v, o_part, lse_part, (int)Nq, (int)Nk, (int)BH, scale, sp.n_splits, sp.split_blocks,
+                     BH * Nq * d, BH * Nq};
+    e = dispatch_d(pr, (int)d, causal != 0, s);
+    if (e == hipSuccess) {
+      const int64_t rows = BH * Nq;
+      const int rpb = 256 / ((int)d / 4);
+      const unsigned blocks = (unsigned)((rows + rpb - 1) / rpb);
+      if (d == 128)
+        hipLaunchKernelGGL(merge_splits<128>, dim3(blocks), dim3(256), 0, s, o_part, lse_part, o, lse, rows,
+                           sp.n_splits, BH * Nq * d, BH * Nq);
+      else
+        hipLaunchKernelGGL(merge_splits<64>, dim3(blocks), dim3(256), 0, s, o_part, lse_part, o, lse, rows,
+                           sp.n_splits, BH * Nq * d, BH * Nq);
+      e = hipGetLastError();
+    }
+  }
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
     return MIFA_ERR_HIP;
@@ -684,13 +858,14 @@ const char* mifa_status_string(int status) {
   switch (status) {
     case MIFA_OK: return "ok";
     case MIFA_ERR_NULL_POINTER: return "null pointer argument";
-    case MIFA_ERR_BAD_SHAPE: return "B, H and N must be >= 1";
+    case MIFA_ERR_BAD_SHAPE: return "B, H, N (Nq, Nk) must be >= 1, and causal needs Nq <= Nk";
     case MIFA_ERR_UNSUPPORTED_D: return "head dimension d must be 64 or 128";
     case MIFA_ERR_MISALIGNED: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
     case MIFA_ERR_BAD_SCALE: return "scale must be finite";
     case MIFA_ERR_TOO_LARGE: return "problem too large (N*d or the tile count reaches 2^31)";
     case MIFA_ERR_HIP: return "HIP runtime error (see mifa_last_hip_error)";
     case MIFA_ERR_BAD_DTYPE: return "dtype must be MIFA_DTYPE_BF16 or MIFA_DTYPE_F32";
+    case MIFA_ERR_WORKSPACE: return "workspace NULL, not 16-byte aligned, or smaller than mifa_splitkv_workspace_bytes";
     default: return "unknown status";
   }
 }

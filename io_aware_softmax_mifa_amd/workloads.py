@@ -17,7 +17,8 @@ import math
 
 import torch
 
-__all__ = ["Workload", "CONFIGS", "by_name", "fp32_scale", "make_inputs", "sample_rows", "SoftmaxWorkload",
+__all__ = ["Workload", "CONFIGS", "by_name", "fp32_scale", "make_inputs", "sample_rows", "DecodeWorkload",
+           "DECODE_CONFIGS", "decode_by_name", "make_rect_inputs", "SoftmaxWorkload",
            "SOFTMAX_CONFIGS", "softmax_by_name", "make_softmax_input", "sample_softmax_rows"]
 
 
@@ -180,3 +181,52 @@ def sample_softmax_rows(rows: int, count: int, seed: int) -> torch.Tensor:
             taken.add(r)
             chosen.append(r)
     return torch.tensor(chosen, dtype=torch.int64)
+
+
+# ---- few queries against many keys (decoding with a key/value cache) ---------------------------
+# The pages give no decoding workload; these stand in for it: the newest Nq positions of a
+# sequence of Nk cached keys, i.i.d. N(0, 1) like the square configurations.
+
+@dataclasses.dataclass(frozen=True)
+class DecodeWorkload:
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    seed: int
+    dist: str = "normal"
+
+
+DECODE_CONFIGS = [
+    # one new token per sequence, 16 sequences of 8 heads with 32K cached keys
+    DecodeWorkload("D1", 16, 8, 1, 32768, 128, True, 301),
+    # a 16-token chunk (speculative / chunked decoding) against 16K keys, 32 heads
+    DecodeWorkload("D2", 1, 32, 16, 16384, 128, True, 302),
+]
+
+
+def decode_by_name(name: str) -> DecodeWorkload:
+    for w in DECODE_CONFIGS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def make_rect_inputs(B: int, H: int, Nq: int, Nk: int, d: int, seed: int, dist: str = "normal"):
+    """bf16 CPU tensors q [B, H, Nq, d], k and v [B, H, Nk, d]; drawn like make_inputs."""
+    g = torch.Generator().manual_seed(seed)
+    sq, skv = (B, H, Nq, d), (B, H, Nk, d)
+    if dist == "normal":
+        q = torch.randn(sq, generator=g)
+        k = torch.randn(skv, generator=g)
+        v = torch.randn(skv, generator=g)
+    elif dist == "stress":
+        q = 2.0 * torch.randn(sq, generator=g)
+        k = 2.0 * torch.randn(skv, generator=g)
+        v = 2.0 * torch.rand(skv, generator=g) - 1.0
+    else:
+        raise ValueError(f"unknown distribution {dist!r}")
+    return (q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16))

@@ -21,7 +21,8 @@ def declared_functions():
 
 
 def test_header_declares_expected_api():
-    assert declared_functions() == ["mifa_fwd", "mifa_last_hip_error", "mifa_softmax_rows", "mifa_status_string",
+    assert declared_functions() == ["mifa_attention", "mifa_attention_splitkv", "mifa_fwd", "mifa_last_hip_error",
+                                    "mifa_softmax_rows", "mifa_splitkv_workspace_bytes", "mifa_status_string",
                                     "mifa_version"]
 
 
@@ -42,7 +43,7 @@ def lib():
 def test_version_and_status_strings(lib):
     assert lib.mifa_version().startswith("mifa ")
     assert "gfx950" in lib.mifa_version()
-    for code in range(9):
+    for code in range(10):
         s = lib.mifa_status_string(code)
         assert s and s != "unknown status"
     assert lib.mifa_status_string(99) == "unknown status"
@@ -143,3 +144,49 @@ def test_softmax_binding_python_checks(lib):
 
     with pytest.raises(ValueError):
         lib.softmax_rows(torch.zeros(2, 8))  # CPU tensors are rejected before any call
+
+
+# ---- mifa_attention and mifa_attention_splitkv -----------------------------------------------
+
+@pytest.mark.parametrize(
+    "args,status",
+    [
+        ((0, A, A, A, A, 1, 1, 4, 64, 64, 0, 0.125), 1),
+        ((A, A, A, A, A, 1, 1, 0, 64, 64, 0, 0.125), 2),
+        ((A, A, A, A, A, 1, 1, 4, 0, 64, 0, 0.125), 2),
+        ((A, A, A, A, A, 1, 1, 65, 64, 64, 1, 0.125), 2),   # causal needs Nq <= Nk
+        ((A, A, A, A, A, 1, 1, 4, 64, 96, 0, 0.125), 3),
+        ((A, A, A + 4, A, A, 1, 1, 4, 64, 64, 0, 0.125), 4),
+        ((A, A, A, A, A, 1, 1, 4, 64, 64, 0, float("nan")), 5),
+        ((A, A, A, A, A, 1, 1, 4, 1 << 24, 128, 0, 0.1), 6),
+    ],
+)
+def test_attention_validation(lib, args, status):
+    got = lib.mifa_attention_raw(*args, None)
+    assert got == status, (args, got, lib.mifa_status_string(got))
+    got = lib.mifa_attention_splitkv_raw(*args, A, 1 << 40, None)
+    assert got == status, (args, got, lib.mifa_status_string(got))
+
+
+def test_attention_accepts_rectangular_noncausal_more_queries(lib):
+    # Nq > Nk is fine without the causal mask: validation passes up to the workspace check
+    assert lib.mifa_attention_splitkv_raw(A, A, A, A, A, 1, 1, 100, 10, 64, 0, 0.1, 0, 0, None) == 9
+
+
+def test_splitkv_workspace_checks(lib):
+    need = lib.mifa_splitkv_workspace_bytes(1, 8, 1, 32768, 128)
+    assert need > 0
+    args = (A, A, A, A, A, 1, 8, 1, 32768, 128, 1, 0.1)
+    assert lib.mifa_attention_splitkv_raw(*args, 0, need, None) == 9          # NULL
+    assert lib.mifa_attention_splitkv_raw(*args, A + 8, need, None) == 9      # misaligned
+    assert lib.mifa_attention_splitkv_raw(*args, A, need - 1, None) == 9      # too small
+    # argument errors come first
+    assert lib.mifa_attention_splitkv_raw(A, A, A, A, A, 1, 8, 2, 1, 128, 1, 0.1, 0, 0, None) == 2
+
+
+def test_splitkv_workspace_bytes(lib):
+    assert lib.mifa_splitkv_workspace_bytes(0, 1, 1, 10, 64) == 0
+    assert lib.mifa_splitkv_workspace_bytes(1, 1, 1, 10, 96) == 0
+    # few queries, many keys: several ranges, each holding O (d floats) and LSE per row
+    n = lib.mifa_splitkv_workspace_bytes(2, 4, 3, 65536, 64)
+    assert n > 0 and n % (2 * 4 * 3 * (64 + 1) * 4) == 0

@@ -720,19 +720,25 @@ hipError_t dispatch_d(const Problem& pr, int d, bool causal, hipStream_t s) {
 
 // ---- merge of key-range partials: the associative rule on (O_s, LSE_s) ----------------------
 // O = sum_s w_s O_s / sum_s w_s and LSE = m + ln sum_s w_s, with w_s = exp(LSE_s - m) and
-// m = max_s LSE_s.  One row per D/4 threads (four O elements each).
+// m = max_s LSE_s.  One row per D/4 threads (four O elements each), 64-thread workgroups so that
+// even a few hundred rows spread over the CUs; the loops over ranges are unrolled so their loads
+// are in flight together.
+constexpr int kMergeThreads = 64;
 template <int D>
-__global__ __launch_bounds__(256) void merge_splits(const float* __restrict__ o_part, const float* __restrict__ lse_part,
-                                                    float* __restrict__ o, float* __restrict__ lse, int64_t rows,
-                                                    int n_splits, int64_t o_split, int64_t lse_split) {
-  constexpr int TPR = D / 4, RPB = 256 / TPR;
+__global__ __launch_bounds__(kMergeThreads) void merge_splits(const float* __restrict__ o_part,
+                                                              const float* __restrict__ lse_part, float* __restrict__ o,
+                                                              float* __restrict__ lse, int64_t rows, int n_splits,
+                                                              int64_t o_split, int64_t lse_split) {
+  constexpr int TPR = D / 4, RPB = kMergeThreads / TPR;
   const int t = threadIdx.x % TPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   if (row >= rows) return;
   float m = -__builtin_inff();
+#pragma unroll 8
   for (int s = 0; s < n_splits; ++s) m = __builtin_elementwise_maximum(m, lse_part[s * lse_split + row]);
   f32x4 acc = {};
   float wsum = 0.f;
+#pragma unroll 8
   for (int s = 0; s < n_splits; ++s) {
     const float ls = lse_part[s * lse_split + row];
     const float w = ls == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((ls - m) * 1.4426950408889634f);
@@ -836,13 +842,13 @@ int mifa_attention_splitkv(const void* q, const void* k, const void* v, float* o
     e = dispatch_d(pr, (int)d, causal != 0, s);
     if (e == hipSuccess) {
       const int64_t rows = BH * Nq;
-      const int rpb = 256 / ((int)d / 4);
+      const int rpb = kMergeThreads / ((int)d / 4);
       const unsigned blocks = (unsigned)((rows + rpb - 1) / rpb);
       if (d == 128)
-        hipLaunchKernelGGL(merge_splits<128>, dim3(blocks), dim3(256), 0, s, o_part, lse_part, o, lse, rows,
+        hipLaunchKernelGGL(merge_splits<128>, dim3(blocks), dim3(kMergeThreads), 0, s, o_part, lse_part, o, lse, rows,
                            sp.n_splits, BH * Nq * d, BH * Nq);
       else
-        hipLaunchKernelGGL(merge_splits<64>, dim3(blocks), dim3(256), 0, s, o_part, lse_part, o, lse, rows,
+        hipLaunchKernelGGL(merge_splits<64>, dim3(blocks), dim3(kMergeThreads), 0, s, o_part, lse_part, o, lse, rows,
                            sp.n_splits, BH * Nq * d, BH * Nq);
       e = hipGetLastError();
     }

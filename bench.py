@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
 KERNEL_SOURCE = os.path.join(ROOT, "io_aware_softmax_mifa_amd", "csrc", "mifa_fwd.hip")
+BWD_SOURCE = os.path.join(ROOT, "io_aware_softmax_mifa_amd", "csrc", "mifa_bwd.hip")
 SOFTMAX_SOURCE = os.path.join(ROOT, "io_aware_softmax_mifa_amd", "csrc", "mifa_softmax.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -342,6 +343,125 @@ def bench_softmax(args):
     print(json.dumps(out), flush=True)
 
 
+def bwd_flops(w) -> float:
+    """Five products per (query, visible key) pair -- S = Q K^T recomputed, dP = dO V^T,
+    dV = P^T dO, dQ = dS K, dK = dS^T Q -- at 2 d FLOPs each: 2.5 times the forward's count
+    (same causal halving)."""
+    return 2.5 * flops(w)
+
+
+def bwd_bytes(w) -> int:
+    """Compulsory bytes: bf16 Q, K, V, dO and fp32 O, LSE read once; fp32 dQ, dK, dV written."""
+    n = w.B * w.H * w.N
+    return 4 * 2 * n * w.d + 4 * n * w.d + 4 * n + 3 * 4 * n * w.d
+
+
+def bench_backward(args):
+    import torch
+
+    from io_aware_softmax_mifa_amd import binding
+    from io_aware_softmax_mifa_amd import workloads as W
+
+    w = W.by_name(args.workload[: -len("-bwd")])
+    scale = W.fp32_scale(w.d)
+    log(f"backward of workload {w.name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} dist={w.dist}")
+    q, k, v = W.make_workload_inputs(w)
+    do = W.make_grad_output(w.B, w.H, w.N, w.d, w.seed)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gq, gk, gv, gdo = (t.to(dev) for t in (q, k, v, do))
+    o, lse = binding.attention(gq, gk, gv, causal=w.causal, scale=scale)
+    dq = torch.empty(w.shape, dtype=torch.float32, device=dev)
+    dk, dv = torch.empty_like(dq), torch.empty_like(dq)
+    need = binding.mifa_bwd_workspace_bytes(w.B, w.H, w.N)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        st = binding.mifa_bwd_raw(gq, gk, gv, o, lse, gdo, dq, dk, dv, w.B, w.H, w.N, w.N, w.d, w.causal, scale,
+                                  ws, ws.numel(), stream.cuda_stream)
+        if st != 0:
+            raise binding.MifaError(st, binding.mifa_status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    call_ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {call_ms:.4f} ms/call (HIP events; "
+        "row_dot + dq + dkdv kernels)")
+    f = bwd_flops(w)
+    value = f / (ms_per_step * 1e-3) / 1e12
+    achieved = f / (call_ms * 1e-3) / 1e12
+    out = {
+        "metric": "attention bwd TFLOP/s (bf16, 2.5x forward FLOP convention) and % of MI355X bf16 MFMA peak",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. bf16 Q/K/V/dO)",
+        "config": {
+            "workload": f"{w.name} backward: B={w.B} H={w.H} N={w.N} d={w.d} causal={int(w.causal)} bf16 Q,K,V,dO "
+                        f"~ N(0,1); fp32 O + LSE from the forward; fp32 dQ, dK, dV",
+            "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": bool(w.causal),
+            "flop_per_step": f,
+            "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
+            "call_ms": call_ms,
+            "compulsory_hbm_bytes": bwd_bytes(w),
+            "workspace_bytes": need,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / PEAK_BF16_TFLOPS,
+            "traffic": measured_traffic(args.workload, BWD_SOURCE),
+            "kernels": "row_dot + dq + dkdv (one mifa_bwd call)",
+        },
+    }
+    if args.no_cpu_baseline:
+        out["cpu_baseline"] = None
+    else:
+        from oracle import attention_bwd_fp64
+
+        heads, L = min(8, w.H), min(4096, w.N)
+        sub = [t[:1, :heads, :L].contiguous() for t in (q, k, v, do)]
+        t0 = time.perf_counter()
+        attention_bwd_fp64(*sub, causal=w.causal, scale=scale)
+        dt = time.perf_counter() - t0
+        pairs = L * L / 2 if w.causal else L * L
+        sample_f = heads * 10.0 * pairs * w.d
+        out["cpu_baseline"] = {
+            "value": sample_f / dt / 1e12,
+            "unit": "TFLOP/s",
+            "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": (f"{heads} heads of batch 0, first {L} positions each (a causal prefix is a complete "
+                       f"smaller problem), float64 NumPy oracle with the full P materialised, {dt:.2f} s; "
+                       f"credited with the same 10 d FLOPs per visible pair"),
+            "seconds": dt,
+            "host_cpus": os.cpu_count(),
+        }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -365,6 +485,8 @@ def main():
         return bench_softmax(args)
     if args.workload.startswith("D"):
         return bench_decode(args)
+    if args.workload.endswith("-bwd"):
+        return bench_backward(args)
 
     import torch
 

@@ -47,7 +47,8 @@ typedef enum mifa_status {
   MIFA_ERR_TOO_LARGE = 6,      /* N*d >= 2^31, or B*H*ceil(N/128) >= 2^31 work tiles */
   MIFA_ERR_HIP = 7,            /* the HIP runtime rejected the launch; see mifa_last_hip_error */
   MIFA_ERR_BAD_DTYPE = 8,      /* dtype is not one of mifa_dtype (mifa_softmax_rows) */
-  MIFA_ERR_WORKSPACE = 9       /* workspace NULL, misaligned or too small (mifa_attention_splitkv) */
+  MIFA_ERR_WORKSPACE = 9       /* workspace NULL, misaligned or too small (mifa_attention_splitkv,
+                                  mifa_bwd) */
 } mifa_status;
 
 /* Element types of mifa_softmax_rows. */
@@ -119,6 +120,41 @@ int mifa_attention_splitkv(const void* q, const void* k, const void* v, float* o
 
 /* Workspace bytes mifa_attention_splitkv needs for this shape (0 for an invalid shape). */
 int64_t mifa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d);
+
+/*
+ * mifa_bwd -- gradients of mifa_attention with respect to q, k and v.
+ *
+ * The pages give the forward only (the ~100-line kernel of "Show HN: Flash Attention in ~100
+ * lines of CUDA" leaves the matrix derivatives out); this is its backward by the chain rule,
+ * with P = softmax(c q k^T [+ causal mask]) recomputed from the saved lse:
+ *     dv = P^T dO,  dP = dO v^T,  D_i = sum_t dO_it o_it,  dS = P * (dP - D),
+ *     dq = c dS k,  dk = c dS^T q.
+ *
+ *   q, k, v, causal, scale, B, H, Nq, Nk, d   exactly as passed to mifa_attention.
+ *   o, lse   float32 [B, H, Nq, d] and [B, H, Nq]: that call's outputs.  Read only.
+ *   dO       bf16 [B, H, Nq, d]: gradient of the loss with respect to o.  Read only.
+ *   dq       float32 [B, H, Nq, d]; dk, dv float32 [B, H, Nk, d].  Fully overwritten.
+ *   workspace  device memory of at least mifa_bwd_workspace_bytes(B, H, Nq) bytes, 16-byte
+ *            aligned; overwritten (it holds D).  Not to be touched until the stream has passed
+ *            the call; calls that share a workspace must be ordered on a stream.
+ *   workspace_bytes  its size in bytes.
+ *   stream   hipStream_t (as void*); NULL for the null stream.
+ * Layouts as for mifa_fwd (d fastest).  q, k, v, o, dO, dq, dk, dv 16-byte aligned; lse 4-byte.
+ * Outputs must not overlap the inputs or each other (not checked).  Rows of a causal problem
+ * that see no key do not occur (Nq <= Nk is required).  The result does not depend on the
+ * launch: no atomics are used, and repeated calls give identical bits.
+ * Errors: as for mifa_attention (NULL_POINTER also for o, dO, dq, dk, dv; MISALIGNED also for
+ * o, dO, dq, dk, dv), plus MIFA_ERR_WORKSPACE, checked last.
+ * Accuracy: products are exact, accumulation is float32, and P and dS are rounded to bf16 before
+ * they multiply dO, q and k.
+ */
+int mifa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse,
+             const void* dO, float* dq, float* dk, float* dv, int64_t B, int64_t H, int64_t Nq,
+             int64_t Nk, int64_t d, int causal, float scale, void* workspace,
+             int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes mifa_bwd needs for this shape (0 for an invalid shape). */
+int64_t mifa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);
 
 /*
  * mifa_softmax_rows -- the row softmax on its own, with the online normaliser.

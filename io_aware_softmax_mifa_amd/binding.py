@@ -30,7 +30,7 @@ STATUS_NAMES = {
 }
 MIFA_DTYPE_BF16, MIFA_DTYPE_F32 = 0, 1
 EXPORTED = ("mifa_fwd", "mifa_attention", "mifa_attention_splitkv", "mifa_splitkv_workspace_bytes",
-            "mifa_softmax_rows", "mifa_status_string", "mifa_version", "mifa_last_hip_error")
+            "mifa_bwd", "mifa_bwd_workspace_bytes", "mifa_softmax_rows", "mifa_status_string", "mifa_version", "mifa_last_hip_error")
 
 
 class MifaError(RuntimeError):
@@ -57,6 +57,11 @@ def _load() -> ctypes.CDLL:
     lib.mifa_attention_splitkv.restype = ctypes.c_int
     lib.mifa_splitkv_workspace_bytes.argtypes = [ctypes.c_int64] * 5
     lib.mifa_splitkv_workspace_bytes.restype = ctypes.c_int64
+    lib.mifa_bwd.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int64] * 5 +
+                             [ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p])
+    lib.mifa_bwd.restype = ctypes.c_int
+    lib.mifa_bwd_workspace_bytes.argtypes = [ctypes.c_int64] * 3
+    lib.mifa_bwd_workspace_bytes.restype = ctypes.c_int64
     lib.mifa_softmax_rows.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_float,
                                                                                       ctypes.c_void_p]
     lib.mifa_softmax_rows.restype = ctypes.c_int
@@ -213,6 +218,46 @@ def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal:
         _raise(mifa_attention_splitkv_raw(q, k, v, out, lse, B, H, Nq, Nk, d, causal, scale, workspace, nbytes,
                                           torch.cuda.current_stream(q.device).cuda_stream))
     return out, lse
+
+
+# ---- the backward ---------------------------------------------------------------------------
+
+def mifa_bwd_raw(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, d, causal, scale, workspace, workspace_bytes,
+                 stream) -> int:
+    """Call the C entry point with raw integer pointers or tensors; returns the status code."""
+    return int(_lib.mifa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk), _ptr(dv),
+                             int(B), int(H), int(Nq), int(Nk), int(d), 1 if causal else 0, float(scale),
+                             _ptr(workspace), int(workspace_bytes), stream or None))
+
+
+def mifa_bwd_workspace_bytes(B, H, Nq) -> int:
+    return int(_lib.mifa_bwd_workspace_bytes(int(B), int(H), int(Nq)))
+
+
+def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                       do: torch.Tensor, causal: bool = False, scale=None, workspace: torch.Tensor | None = None):
+    """Gradients (dq, dk, dv), float32 shaped like q, k, v, of attention(q, k, v, causal, scale)
+    for the upstream gradient do (bf16, shaped like q); o and lse are that forward's outputs.
+    `workspace`: a GPU tensor of at least mifa_bwd_workspace_bytes(B, H, Nq) bytes, allocated
+    here (uint8) unless given.  Asynchronous on torch's current stream."""
+    B, H, Nq, Nk, d = _qkv(q, k, v)
+    _check("do", do, (B, H, Nq, d))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    for name, t, shape in (("o", o, (B, H, Nq, d)), ("lse", lse, (B, H, Nq))):
+        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous float32 {shape} tensor on q's device")
+    dq = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+    dk = torch.empty((B, H, Nk, d), dtype=torch.float32, device=q.device)
+    dv = torch.empty((B, H, Nk, d), dtype=torch.float32, device=q.device)
+    need = mifa_bwd_workspace_bytes(B, H, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    nbytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        _raise(mifa_bwd_raw(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, d, causal, scale, workspace, nbytes,
+                            torch.cuda.current_stream(q.device).cuda_stream))
+    return dq, dk, dv
 
 
 # ---- the row softmax ------------------------------------------------------------------------

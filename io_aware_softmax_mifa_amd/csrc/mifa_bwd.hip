@@ -1,0 +1,515 @@
+// mifa_bwd.hip -- gradients of exact attention for MI355X (gfx950).
+//
+// What is computed: for the forward O = P V, P = softmax(S) row by row, S = c Q K^T (the causal
+// variant masks key j for query i iff j > i + Nk - Nq) and an upstream gradient dO,
+//     dV = P^T dO,   dP = dO V^T,   D_i = sum_t dO_it O_it,   dS = P * (dP - D),
+//     dQ = c dS K,   dK = c dS^T Q.
+// The pages stop at the forward pass ("Show HN: Flash Attention in ~100 lines of CUDA" leaves
+// the matrix derivatives out); this is the next step, built the same way as the forward: fused
+// and tiled, with P recomputed block by block from the forward's saved LSE
+// (P_ij = exp(c s_ij - LSE_i)) instead of being stored, so no N x N matrix reaches HBM.
+//
+// Three kernels, no atomics (results are bitwise reproducible):
+//  * row_dot: D_i = dO_i . O_i per query row (one pass over O and dO).
+//  * dq: one workgroup per (b*h, 128-query tile), like the forward: each wave keeps 32 query
+//    rows of Q and dO in registers, streams K and V blocks of 64 keys through LDS, computes
+//    S^T = K Q^T and dP^T = V dO^T on MFMA, then dS^T, and accumulates dQ^T += K^T dS^T (K^T
+//    read from the K tile with the transposing LDS read).
+//  * dkdv: one workgroup per (b*h, 128-key tile), the roles swapped: each wave keeps 32 keys
+//    of K and V in registers, streams Q and dO blocks of 64 queries (with their LSE and D),
+//    computes S = Q K^T and dP = dO V^T, then P and dS, and accumulates dV^T += dO^T P and
+//    dK^T += Q^T dS.
+// In both, the probabilities / dS feed the second product straight from the accumulator
+// layout (the contraction index inside one MFMA is a free permutation), as in the forward.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+#include "mifa.h"
+#include "mifa_common.h"
+
+namespace {
+
+using namespace mifa_detail;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;  // rows (queries or keys) a workgroup owns
+constexpr int kBlk = 64;            // rows of a streamed block (keys or queries)
+
+template <int D>
+struct Geo {
+  static constexpr int kDS = D / 16;                // 16-wide d slices
+  static constexpr int kDT = D / 32;                // 32-row d tiles of a transposed product
+  static constexpr int kTile = kBlk * D * 2;        // bytes of one bf16 block
+  static constexpr int kChunksPerRow = D / 8;       // 16-byte chunks per row
+  static constexpr int kRowsPerInst = 64 / kChunksPerRow;
+  static constexpr int kInstPerTile = kBlk / kRowsPerInst;
+  static constexpr int kInstPerWave = kInstPerTile / kWaves;
+  static constexpr int kLds = 2 * 2 * kTile;        // two tensors, double buffered
+  static_assert(kInstPerWave * kWaves == kInstPerTile, "tile splits evenly over the waves");
+};
+
+// ---- tiles in LDS --------------------------------------------------------------------------
+// A block of kBlk rows x D bf16, rows of D*2 bytes, 16-byte chunk c of row r at c ^ swz_k(r).
+// DMA instruction t of this wave covers rows (wave*kInstPerWave + t)*kRowsPerInst ...; rows past
+// row_limit are clamped to it (the last, partial block).
+template <int D>
+__device__ __forceinline__ void dma_tile(const __bf16* src, char* dst, int wave, int lane, int row_limit) {
+  using G = Geo<D>;
+  const char* s = (const char*)src;
+#pragma unroll
+  for (int t = 0; t < G::kInstPerWave; ++t) {
+    const int inst = wave * G::kInstPerWave + t;
+    const int r = inst * G::kRowsPerInst + lane / G::kChunksPerRow;
+    const int pc = lane % G::kChunksPerRow;
+    const int rr = r < row_limit ? r : row_limit;
+    const unsigned off = (unsigned)(rr * (D * 2) + ((pc ^ swz_k<D>(r)) * 16));
+    __builtin_amdgcn_global_load_lds((global_cvoid*)(s + off), (lds_void*)(dst + inst * 1024), 16, 0, 0);
+  }
+}
+template <int D>
+constexpr int dma_ops() {
+  return Geo<D>::kInstPerWave;
+}
+
+// Row-major operand read (A operand of X Y^T, X the tile): lane l reads row l%32 (+32*rt) of
+// the tile at logical chunk 2s + l/32.  base = this lane's row address in tile 0, chunk part
+// applied here.
+template <int D>
+__device__ __forceinline__ unsigned row_addr(unsigned tile, int row, int s, int hf) {
+  return tile + row * (D * 2) + ((((2 * s + hf) ^ swz_k<D>(row))) * 16);
+}
+
+// Transposing operand read (A operand of X^T Y): lane (g = lane/16, p = lane%16) reads, for
+// column tile t, the 4 rows r = 4 hf + p/4 (+8 for the high half, +16 ks) at column chunk
+// 4t + 2(g%2) + (p%4)/2, byte (p%2)*8.  Each 16-lane group then holds one column of 4 rows.
+template <int D>
+__device__ __forceinline__ unsigned tr_addr(unsigned tile, int lane, int t, int hi) {
+  const int g = lane >> 4, p = lane & 15, hf = lane >> 5;
+  const int r = 4 * hf + (p >> 2) + 8 * hi;
+  const int cl = 2 * (g & 1) + ((p & 3) >> 1);
+  return tile + r * (D * 2) + (p & 1) * 8 + (((4 * t + cl) ^ swz_k<D>(r)) * 16);
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Load 32 rows x D of a bf16 [rows, D] tensor into the B-operand layout of a 32x32x16 MFMA:
+// lane l holds row l%32, elements 16s + 8(l/32) .. +7 of slice s.  Rows at or past `rows`
+// are clamped; flip = 1 negates (sign bit) every element.
+template <int D>
+__device__ __forceinline__ void load_rows(const __bf16* base, int row, int rows, int hf, int flip,
+                                          bf16x8 (&f)[D / 16]) {
+  const int r = row < rows ? row : rows - 1;
+  const __bf16* src = base + (int64_t)r * D + 8 * hf;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    u32x4 raw = *(const u32x4*)(src + 16 * s);
+    if (flip) raw ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    f[s] = __builtin_bit_cast(bf16x8, raw);
+  }
+}
+
+// Pack a 32x32 accumulator pair (two 32-row tiles along the contraction) into the B operand of
+// the following product: slice ks (16 contraction rows) takes elements 8(ks%2) .. +7 of tile
+// ks/2, converted to bf16.
+__device__ __forceinline__ void pack(const f32x16 (&x)[2], bf16x8 (&pb)[4]) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pb[2 * tt + (i >> 3)][i & 7] = (__bf16)x[tt][i];
+}
+
+// Store a transposed accumulator (lane = output row, 16 values of a 32-column tile t) scaled by
+// `mul` to row `row` of a float [rows, D] tensor.
+template <int D>
+__device__ __forceinline__ void store_row(float* base, int row, int hf, const f32x16 (&acc)[D / 32], float mul) {
+  float* dst = base + (int64_t)row * D;
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 v = {acc[t][4 * g4] * mul, acc[t][4 * g4 + 1] * mul, acc[t][4 * g4 + 2] * mul,
+                       acc[t][4 * g4 + 3] * mul};
+      *(f32x4*)(dst + 32 * t + 8 * g4 + 4 * hf) = v;
+    }
+}
+
+// Row-major A-operand products of the two 32-row tiles of a block with the wave's registers:
+// acc[tt] = sum_s tile[rows 32 tt + l%32][slice s] (x) f[s].  All reads of a tile are issued
+// first; each MFMA waits only for its own operand (LDS reads complete in order).
+template <int D, int S>
+__device__ __forceinline__ void rm_step(bf16x8 (&a)[D / 16], const bf16x8 (&f)[D / 16], f32x16& acc, IC<S>) {
+  lgkm_wait<D / 16 - 1 - S>(a[S]);
+  acc = mfma(a[S], f[S], S == 0 ? (f32x16){} : acc);
+}
+template <int D>
+__device__ __forceinline__ void rowmajor_tile(unsigned tile, int row, int hf, const bf16x8 (&f)[D / 16], f32x16& acc) {
+  bf16x8 a[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) a[s] = lds_read_b128<0>(row_addr<D>(tile, row, s, hf));
+  [&]<int... S>(std::integer_sequence<int, S...>) { (rm_step<D>(a, f, acc, IC<S>{}), ...); }(
+      std::make_integer_sequence<int, D / 16>{});
+}
+template <int D>
+__device__ __forceinline__ void rowmajor_products(unsigned tile, int ln, int hf, const bf16x8 (&f)[D / 16],
+                                                  f32x16 (&acc)[2]) {
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) rowmajor_tile<D>(tile, 32 * tt + ln, hf, f, acc[tt]);
+}
+
+// Transposed A-operand products: acc[t] += tile^T[cols 32 t ..][rows 16 ks ..] (x) pb[ks], the
+// 16 contraction rows of slice ks in the order the accumulator layout hands them over.
+template <int D, int KS, int NP>
+__device__ __forceinline__ void tp_step(const unsigned (&tra)[D / 32][2], const bf16x8 (&pb)[NP],
+                                        f32x16 (&acc)[D / 32], int pidx, IC<KS>) {
+  constexpr int kDT = D / 32, off = KS * 16 * D * 2;
+  i16x4 lo[kDT], hi[kDT];
+#pragma unroll
+  for (int t = 0; t < kDT; ++t) {
+    lo[t] = lds_read_tr<off>(tra[t][0]);
+    hi[t] = lds_read_tr<off>(tra[t][1]);
+  }
+  [&]<int... T>(std::integer_sequence<int, T...>) {
+    ((lgkm_wait<2 * (kDT - 1 - T)>(lo[T], hi[T]),
+      acc[T] = mfma(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[T], hi[T], 0, 1, 2, 3, 4, 5, 6, 7)),
+                    pb[pidx], acc[T])),
+     ...);
+  }(std::make_integer_sequence<int, kDT>{});
+}
+template <int D>
+__device__ __forceinline__ void transposed_products(const unsigned (&tra)[D / 32][2], const bf16x8 (&pb)[4],
+                                                    f32x16 (&acc)[D / 32]) {
+  [&]<int... KS>(std::integer_sequence<int, KS...>) { (tp_step<D>(tra, pb, acc, KS, IC<KS>{}), ...); }(
+      std::make_integer_sequence<int, 4>{});
+}
+// Slices 2 TT and 2 TT + 1 only (one 32-row tile of the contraction), pb holding those two.
+template <int D, int TT>
+__device__ __forceinline__ void transposed_products_tile(const unsigned (&tra)[D / 32][2], const bf16x8 (&pb)[2],
+                                                         f32x16 (&acc)[D / 32]) {
+  tp_step<D>(tra, pb, acc, 0, IC<2 * TT>{});
+  tp_step<D>(tra, pb, acc, 1, IC<2 * TT + 1>{});
+}
+
+template <int D>
+__device__ __forceinline__ void tr_addrs(unsigned tile, int lane, unsigned (&tra)[D / 32][2]) {
+#pragma unroll
+  for (int t = 0; t < D / 32; ++t) {
+    tra[t][0] = tr_addr<D>(tile, lane, t, 0);
+    tra[t][1] = tr_addr<D>(tile, lane, t, 1);
+  }
+}
+
+// ---- launch parameters ------------------------------------------------------------------------
+struct BwdParams {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* dO;
+  const float* lse;   // forward LSE, [BH, Nq]
+  const float* dd;    // D = rowsum(dO * O), [BH, Nq]
+  float* dq;
+  float* dk;
+  float* dv;
+  int Nq, Nk, BH;
+  float c_log2;       // |scale| * log2(e)
+  float scale;        // signed, for dQ and dK
+  int negate;         // scale < 0: the sign is moved onto Q (dq kernel) or K (dkdv kernel)
+};
+
+// ---- D = rowsum(dO * O) --------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void row_dot_kernel(const __bf16* __restrict__ dO, const float* __restrict__ o,
+                                                     float* __restrict__ dd, int64_t rows) {
+  constexpr int TPR = D / 4, RPB = 64 / TPR;
+  const int t = threadIdx.x % TPR;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  float s = 0.f;
+  if (row < rows) {
+    const f32x4 ov = *(const f32x4*)(o + row * D + 4 * t);
+    const uint64_t raw = *(const uint64_t*)(dO + row * D + 4 * t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += __builtin_bit_cast(float, (unsigned)((raw >> (16 * i)) & 0xffffu) << 16) * ov[i];
+  }
+#pragma unroll
+  for (int off = TPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, TPR);
+  if (row < rows && t == 0) dd[row] = s;
+}
+
+// ---- dQ ------------------------------------------------------------------------------------
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void dq_kernel(BwdParams p) {
+  using G = Geo<D>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, ln = lane & 31, hf = lane >> 5;
+  const int BH = p.BH, Nq = p.Nq, Nk = p.Nk, kshift = Nk - Nq;
+  const int bh = blockIdx.x % BH, qt = blockIdx.x / BH;
+  const int my_row = qt * kRows + wave * 32 + ln;
+
+  bf16x8 qf[G::kDS], dof[G::kDS];
+  load_rows<D>(p.q + (int64_t)bh * Nq * D, my_row, Nq, hf, p.negate, qf);
+  load_rows<D>(p.dO + (int64_t)bh * Nq * D, my_row, Nq, hf, 0, dof);
+  const int rc = my_row < Nq ? my_row : Nq - 1;
+  const float lse2 = p.lse[(int64_t)bh * Nq + rc] * 1.4426950408889634f;
+  const float drow = p.dd[(int64_t)bh * Nq + rc];
+  f32x16 acc[G::kDT];
+#pragma unroll
+  for (int t = 0; t < G::kDT; ++t) acc[t] = (f32x16){};
+
+  const int n_kb = (Nk + kBlk - 1) / kBlk;
+  int nblk = n_kb, j_mask = Nk / kBlk;
+  if (CAUSAL) {
+    const int last_row = min(Nq - 1, qt * kRows + kRows - 1);
+    nblk = min(n_kb, (last_row + kshift) / kBlk + 1);
+    j_mask = min(j_mask, (qt * kRows + kshift) / kBlk);
+  }
+  const __bf16* kh = p.k + (int64_t)bh * Nk * D;
+  const __bf16* vh = p.v + (int64_t)bh * Nk * D;
+  const unsigned base = (unsigned)(uintptr_t)(lds_void*)smem;
+  const int my_pos = my_row + kshift;
+
+  // Buffer b holds K at smem + 2b kTile and V at smem + (2b + 1) kTile.
+  dma_tile<D>(kh, smem, wave, lane, Nk - 1);
+  dma_tile<D>(vh, smem + G::kTile, wave, lane, Nk - 1);
+  for (int j = 0; j < nblk; ++j) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();  // block j has landed for every wave; block j-1 is done
+    const int b = j & 1;
+    if (j + 1 < nblk) {
+      const int nb = (j + 1) & 1;
+      const int limit = Nk - 1 - (j + 1) * kBlk;
+      dma_tile<D>(kh + (int64_t)(j + 1) * kBlk * D, smem + 2 * nb * G::kTile, wave, lane, limit);
+      dma_tile<D>(vh + (int64_t)(j + 1) * kBlk * D, smem + (2 * nb + 1) * G::kTile, wave, lane, limit);
+    }
+    const unsigned kt_base = base + 2 * b * G::kTile, vt_base = kt_base + G::kTile;
+    f32x16 s[2], dp[2];
+    rowmajor_products<D>(kt_base, ln, hf, qf, s);
+    rowmajor_products<D>(vt_base, ln, hf, dof, dp);
+    const int key0 = j * kBlk;
+    if (j >= j_mask) {
+      int lim = Nk - 1 - key0 - 4 * hf;
+      if (CAUSAL) lim = min(lim, my_pos - key0 - 4 * hf);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * kt + 8 * (i >> 2) + (i & 3) > lim) s[kt][i] = -__builtin_inff();
+    }
+    f32x16 ds[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][i], p.c_log2, -lse2));
+        ds[kt][i] = pr * (dp[kt][i] - drow);
+      }
+    bf16x8 dsb[4];
+    pack(ds, dsb);
+    unsigned tra[G::kDT][2];
+    tr_addrs<D>(kt_base, lane, tra);
+    transposed_products<D>(tra, dsb, acc);
+  }
+  wait_vmcnt<0>();
+  if (my_row < Nq) store_row<D>(p.dq + (int64_t)bh * Nq * D, my_row, hf, acc, p.scale);
+}
+
+// ---- dK, dV -------------------------------------------------------------------------------
+// One 32-query tile TT of a query block: S = Q K^T and dP = dO V^T for the wave's 32 keys, then
+// P and dS, then dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries.
+template <int D, bool CAUSAL, int TT>
+__device__ __forceinline__ void block_tile(unsigned qt_base, unsigned dot_base, unsigned rv, int ln, int hf,
+                                           const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16], bool masked, int q0,
+                                           int Nq, int my_key, int kshift, float c_log2,
+                                           const unsigned (&tra_do)[D / 32][2], const unsigned (&tra_q)[D / 32][2],
+                                           f32x16 (&dv)[D / 32], f32x16 (&dk)[D / 32]) {
+  f32x16 s, dp;
+  rowmajor_tile<D>(qt_base, 32 * TT + ln, hf, kf, s);
+  rowmajor_tile<D>(dot_base, 32 * TT + ln, hf, vf, dp);
+  f32x4 lv[4], dvv[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const unsigned ra = rv + (32 * TT + 8 * g + 4 * hf) * 4;
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:256\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(lv[g]), "=v"(dvv[g]) : "v"(ra));
+  }
+  bf16x8 pb[2], dsb[2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float sv = s[i];
+    if (masked) {
+      const int qg = q0 + 32 * TT + 8 * (i >> 2) + 4 * hf + (i & 3);
+      const bool vis = qg < Nq && (!CAUSAL || my_key <= qg + kshift);
+      sv = vis ? sv : -__builtin_inff();
+    }
+    const float l2 = lv[i >> 2][i & 3] * 1.4426950408889634f;
+    const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c_log2, -l2));
+    pb[i >> 3][i & 7] = (__bf16)pr;
+    dsb[i >> 3][i & 7] = (__bf16)(pr * (dp[i] - dvv[i >> 2][i & 3]));
+  }
+  transposed_products_tile<D, TT>(tra_do, pb, dv);
+  transposed_products_tile<D, TT>(tra_q, dsb, dk);
+}
+
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2)))
+void dkdv_kernel(BwdParams p) {
+  using G = Geo<D>;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, ln = lane & 31, hf = lane >> 5;
+  const int BH = p.BH, Nq = p.Nq, Nk = p.Nk, kshift = Nk - Nq;
+  const int bh = blockIdx.x % BH, kb = blockIdx.x / BH;
+  const int tile_key0 = kb * kRows;
+  const int my_key = tile_key0 + wave * 32 + ln;
+
+  bf16x8 kf[G::kDS], vf[G::kDS];
+  load_rows<D>(p.k + (int64_t)bh * Nk * D, my_key, Nk, hf, p.negate, kf);
+  load_rows<D>(p.v + (int64_t)bh * Nk * D, my_key, Nk, hf, 0, vf);
+  f32x16 dv[G::kDT], dk[G::kDT];
+#pragma unroll
+  for (int t = 0; t < G::kDT; ++t) dv[t] = dk[t] = (f32x16){};
+
+  // Query blocks [jb, n_qb): with the causal mask a query sees this tile's keys only from
+  // position tile_key0 on.  Blocks whose first query sits before the tile's last key, and the
+  // last partial block, take the masked path.
+  const int n_qb = (Nq + kBlk - 1) / kBlk;
+  int jb = 0;
+  if (CAUSAL) jb = max(0, tile_key0 - kshift) / kBlk;
+  const __bf16* qh = p.q + (int64_t)bh * Nq * D;
+  const __bf16* doh = p.dO + (int64_t)bh * Nq * D;
+  const float* lh = p.lse + (int64_t)bh * Nq;
+  const float* dh = p.dd + (int64_t)bh * Nq;
+  const unsigned base = (unsigned)(uintptr_t)(lds_void*)smem;
+  // LDS: buffer b holds Q at smem + 2b kTile, dO at smem + (2b + 1) kTile; the rows' LSE and D
+  // follow the four tiles (64 floats each, two buffers).
+  char* rowvals = smem + 4 * G::kTile;
+  auto load_block = [&](int jq, int buf) {
+    const int limit = Nq - 1 - jq * kBlk;
+    dma_tile<D>(qh + (int64_t)jq * kBlk * D, smem + 2 * buf * G::kTile, wave, lane, limit);
+    dma_tile<D>(doh + (int64_t)jq * kBlk * D, smem + (2 * buf + 1) * G::kTile, wave, lane, limit);
+    if (wave == 0) {
+      const int r = lane < limit ? lane : limit;
+      __builtin_amdgcn_global_load_lds((global_cvoid*)(lh + (int64_t)jq * kBlk + r), (lds_void*)(rowvals + buf * 512),
+                                       4, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_cvoid*)(dh + (int64_t)jq * kBlk + r),
+                                       (lds_void*)(rowvals + buf * 512 + 256), 4, 0, 0);
+    }
+  };
+  if (jb < n_qb) load_block(jb, 0);
+  for (int jq = jb; jq < n_qb; ++jq) {
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    const int b = (jq - jb) & 1;
+    if (jq + 1 < n_qb) load_block(jq + 1, b ^ 1);
+    const unsigned qt_base = base + 2 * b * G::kTile, dot_base = qt_base + G::kTile;
+    // this lane's 16 query rows of tile tt: 32 tt + 8 g + 4 hf + (0..3), g = 0..3
+    const unsigned rv = base + 4 * G::kTile + b * 512;
+    const int q0 = jq * kBlk;
+    const bool masked = (CAUSAL && q0 + kshift < tile_key0 + kRows - 1) || q0 + kBlk > Nq;
+    unsigned tra_do[G::kDT][2], tra_q[G::kDT][2];
+    tr_addrs<D>(dot_base, lane, tra_do);
+    tr_addrs<D>(qt_base, lane, tra_q);
+    [&]<int... TT>(std::integer_sequence<int, TT...>) {
+      ((block_tile<D, CAUSAL, TT>(qt_base, dot_base, rv, ln, hf, kf, vf, masked, q0, Nq, my_key, kshift, p.c_log2,
+                                  tra_do, tra_q, dv, dk)),
+       ...);
+    }(std::make_integer_sequence<int, 2>{});
+  }
+  wait_vmcnt<0>();
+  if (my_key < Nk) {
+    store_row<D>(p.dv + (int64_t)bh * Nk * D, my_key, hf, dv, 1.f);
+    store_row<D>(p.dk + (int64_t)bh * Nk * D, my_key, hf, dk, p.scale);
+  }
+}
+
+constexpr int kRowValsBytes = 2 * 512;
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd(const BwdParams& p, const float* o, float* dd, hipStream_t s) {
+  using G = Geo<D>;
+  const int64_t rows = (int64_t)p.BH * p.Nq;
+  constexpr int rpb = 64 / (D / 4);
+  hipLaunchKernelGGL(row_dot_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(64), 0, s, p.dO, o, dd, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  static const hipError_t a1 =
+      hipFuncSetAttribute((const void*)dq_kernel<D, CAUSAL>, hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
+  static const hipError_t a2 = hipFuncSetAttribute((const void*)dkdv_kernel<D, CAUSAL>,
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds + kRowValsBytes);
+  if (a1 != hipSuccess) return a1;
+  if (a2 != hipSuccess) return a2;
+  const unsigned gq = (unsigned)((int64_t)p.BH * ((p.Nq + kRows - 1) / kRows));
+  const unsigned gk = (unsigned)((int64_t)p.BH * ((p.Nk + kRows - 1) / kRows));
+  hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(gq), dim3(kThreads), G::kLds, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(gk), dim3(kThreads), G::kLds + kRowValsBytes, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" __attribute__((visibility("hidden"))) void mifa_record_hip_error(int e);
+
+extern "C" int64_t mifa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq) {
+  if (B < 1 || H < 1 || Nq < 1 || B > ((int64_t)1 << 31) || H > ((int64_t)1 << 31)) return 0;
+  return B * H * Nq * 4;
+}
+
+extern "C" int mifa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dO,
+                        float* dq, float* dk, float* dv, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                        int causal, float scale, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return MIFA_ERR_NULL_POINTER;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (causal && Nq > Nk)) return MIFA_ERR_BAD_SHAPE;
+  if (d != 64 && d != 128) return MIFA_ERR_UNSUPPORTED_D;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dO | (uintptr_t)dq | (uintptr_t)dk |
+       (uintptr_t)dv) & 15u)
+    return MIFA_ERR_MISALIGNED;
+  if ((uintptr_t)lse & 3u) return MIFA_ERR_MISALIGNED;
+  if (!__builtin_isfinite(scale)) return MIFA_ERR_BAD_SCALE;
+  if (Nq * d >= ((int64_t)1 << 31) || Nk * d >= ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
+  if (B > ((int64_t)1 << 31) || H > ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
+  const int64_t BH = B * H;
+  if (BH >= ((int64_t)1 << 31) || BH * ((Nq + 127) / 128) >= ((int64_t)1 << 31) ||
+      BH * ((Nk + 127) / 128) >= ((int64_t)1 << 31))
+    return MIFA_ERR_TOO_LARGE;
+  if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes < BH * Nq * 4) return MIFA_ERR_WORKSPACE;
+
+  BwdParams p;
+  p.q = (const __bf16*)q;
+  p.k = (const __bf16*)k;
+  p.v = (const __bf16*)v;
+  p.dO = (const __bf16*)dO;
+  p.lse = lse;
+  p.dd = (const float*)workspace;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.BH = (int)BH;
+  p.negate = scale < 0.f ? 1 : 0;
+  double c_exact = (double)(p.negate ? -scale : scale) * 1.4426950408889634;
+  if (c_exact < 1e-30) c_exact = 1e-30;
+  p.c_log2 = (float)c_exact;
+  p.scale = scale;
+  hipStream_t s = (hipStream_t)stream;
+  float* dd = (float*)workspace;
+  hipError_t e;
+  if (d == 128)
+    e = causal ? launch_bwd<128, true>(p, o, dd, s) : launch_bwd<128, false>(p, o, dd, s);
+  else
+    e = causal ? launch_bwd<64, true>(p, o, dd, s) : launch_bwd<64, false>(p, o, dd, s);
+  if (e != hipSuccess) {
+    mifa_record_hip_error((int)e);
+    return MIFA_ERR_HIP;
+  }
+  return MIFA_OK;
+}

@@ -230,3 +230,9 @@ def make_rect_inputs(B: int, H: int, Nq: int, Nk: int, d: int, seed: int, dist: 
     else:
         raise ValueError(f"unknown distribution {dist!r}")
     return (q.to(torch.bfloat16), k.to(torch.bfloat16), v.to(torch.bfloat16))
+
+
+def make_grad_output(B: int, H: int, Nq: int, d: int, seed: int) -> torch.Tensor:
+    """bf16 CPU tensor dO [B, H, Nq, d] ~ N(0, 1): the upstream gradient of a backward pass."""
+    g = torch.Generator().manual_seed(seed + 7919)
+    return torch.randn((B, H, Nq, d), generator=g).to(torch.bfloat16)

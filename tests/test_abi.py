@@ -21,9 +21,9 @@ def declared_functions():
 
 
 def test_header_declares_expected_api():
-    assert declared_functions() == ["mifa_attention", "mifa_attention_splitkv", "mifa_fwd", "mifa_last_hip_error",
-                                    "mifa_softmax_rows", "mifa_splitkv_workspace_bytes", "mifa_status_string",
-                                    "mifa_version"]
+    assert declared_functions() == ["mifa_attention", "mifa_attention_splitkv", "mifa_bwd", "mifa_bwd_workspace_bytes",
+                                    "mifa_fwd", "mifa_last_hip_error", "mifa_softmax_rows",
+                                    "mifa_splitkv_workspace_bytes", "mifa_status_string", "mifa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -190,3 +190,41 @@ def test_splitkv_workspace_bytes(lib):
     # few queries, many keys: several ranges, each holding O (d floats) and LSE per row
     n = lib.mifa_splitkv_workspace_bytes(2, 4, 3, 65536, 64)
     assert n > 0 and n % (2 * 4 * 3 * (64 + 1) * 4) == 0
+
+
+# ---- mifa_bwd --------------------------------------------------------------------------------
+
+def _bwd(lib, q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, B=1, H=2, Nq=100, Nk=100, d=128, causal=1,
+         scale=0.1, ws=A, wsb=1 << 40):
+    return lib.mifa_bwd_raw(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, d, causal, scale, ws, wsb, None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(q=0), 1), (dict(o=0), 1), (dict(lse=0), 1), (dict(do=0), 1), (dict(dq=0), 1), (dict(dk=0), 1),
+        (dict(dv=0), 1),
+        (dict(B=0), 2), (dict(Nq=0), 2), (dict(Nk=0), 2), (dict(Nq=101), 2),
+        (dict(d=96), 3),
+        (dict(do=A + 8), 4), (dict(dk=A + 4), 4), (dict(o=A + 2), 4), (dict(lse=A + 2), 4),
+        (dict(scale=float("inf")), 5),
+        (dict(Nq=1 << 24, Nk=1 << 24), 6),
+        (dict(ws=0), 9), (dict(ws=A + 8), 9), (dict(wsb=2 * 100 * 4 - 1), 9),
+    ],
+)
+def test_bwd_validation(lib, kw, status):
+    got = _bwd(lib, **kw)
+    assert got == status, (kw, got, lib.mifa_status_string(got))
+
+
+def test_bwd_validation_order(lib):
+    assert _bwd(lib, q=0, Nq=0, ws=0) == 1      # NULL before shape
+    assert _bwd(lib, Nq=0, d=96) == 2            # shape before d
+    assert _bwd(lib, d=96, q=A + 2) == 3         # d before alignment
+    assert _bwd(lib, scale=float("nan"), ws=0) == 5  # arguments before the workspace
+    assert _bwd(lib, causal=0, Nq=101, ws=0) == 9    # Nq > Nk is fine without the causal mask
+
+
+def test_bwd_workspace_bytes(lib):
+    assert lib.mifa_bwd_workspace_bytes(0, 1, 1) == 0
+    assert lib.mifa_bwd_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 4

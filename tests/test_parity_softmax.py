@@ -4,7 +4,7 @@ CPU oracle.
 Tolerances, derived from the arithmetic: the kernel works in fp32 (one FMA for c*x, v_exp_f32,
 fp32 sums of at most 64 terms per thread then a tree, one reciprocal), so an fp32 output is
 within a few 1e-6 relative of the exact value; the bar is 3e-5 relative.  A bf16 output adds
-one round-to-nearest-even (2^-9 relative), so its bar is 4e-3 relative.  LSE is fp32 with
+one round-to-nearest-even (at most 2^-8 relative: 8 significant bits), so its bar is 4e-3 relative.  LSE is fp32 with
 the max exact up to the product rounding: 2e-5 absolute plus 1e-6 relative.  Outputs that
 underflow fp32 are compared with an absolute floor of 1e-30.
 """

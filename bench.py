@@ -441,7 +441,7 @@ def bench_backward(args):
     else:
         from oracle import attention_bwd_fp64
 
-        heads, L = min(8, w.H), min(4096, w.N)
+        heads, L = min(16, w.H), min(8192, w.N)
         sub = [t[:1, :heads, :L].contiguous() for t in (q, k, v, do)]
         t0 = time.perf_counter()
         attention_bwd_fp64(*sub, causal=w.causal, scale=scale)

@@ -42,13 +42,15 @@ typedef enum mifa_status {
   MIFA_ERR_NULL_POINTER = 1,   /* q, k, v, o or lse is NULL */
   MIFA_ERR_BAD_SHAPE = 2,      /* B, H or N (Nq, Nk) < 1, or causal with Nq > Nk */
   MIFA_ERR_UNSUPPORTED_D = 3,  /* head dimension d is not 64 or 128 */
-  MIFA_ERR_MISALIGNED = 4,     /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
+  MIFA_ERR_MISALIGNED = 4,     /* a tensor not 16-byte aligned (lse: 4-byte), or a stride not a
+                                  multiple of 8 elements */
   MIFA_ERR_BAD_SCALE = 5,      /* scale is NaN or infinite */
   MIFA_ERR_TOO_LARGE = 6,      /* N*d >= 2^31, or B*H*ceil(N/128) >= 2^31 work tiles */
   MIFA_ERR_HIP = 7,            /* the HIP runtime rejected the launch; see mifa_last_hip_error */
   MIFA_ERR_BAD_DTYPE = 8,      /* dtype is not one of mifa_dtype (mifa_softmax_rows) */
-  MIFA_ERR_WORKSPACE = 9       /* workspace NULL, misaligned or too small (mifa_attention_splitkv,
+  MIFA_ERR_WORKSPACE = 9,      /* workspace NULL, misaligned or too small (mifa_attention_splitkv,
                                   mifa_bwd) */
+  MIFA_ERR_BAD_STRIDE = 10     /* a stride is negative (the *_strided entry points) */
 } mifa_status;
 
 /* Element types of mifa_softmax_rows. */
@@ -95,6 +97,29 @@ int mifa_fwd(const void* q, const void* k, const void* v, float* o, float* lse,
 int mifa_attention(const void* q, const void* k, const void* v, float* o, float* lse,
                    int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
                    void* stream);
+
+/*
+ * mifa_attention_strided -- mifa_attention on tensors of any (batch, head, row) strides, with O
+ * in float32 or bf16: the layouts of the scaled-dot-product-attention call the Hacker News
+ * FlashAttention-3 thread names as the user-facing entry ([B, H, N, d], or [B, N, H, d] views
+ * of one projection output) are read in place, without copies.
+ *
+ *   strides  host array of 12 int64: the (batch, head, row) strides, in elements, of q, k, v
+ *            and o in that order.  Element (b,h,i,t) of q lives at
+ *            q[b*strides[0] + h*strides[1] + i*strides[2] + t]; d is contiguous.  Strides must
+ *            be >= 0 (MIFA_ERR_BAD_STRIDE) and multiples of 8 (MIFA_ERR_MISALIGNED); row
+ *            strides below 2^24 (MIFA_ERR_TOO_LARGE).  A zero stride on q, k or v broadcasts
+ *            it; o must not overlap itself or the inputs (not checked).
+ *   o_dtype  MIFA_DTYPE_F32 or MIFA_DTYPE_BF16 (rounded to nearest even); MIFA_ERR_BAD_DTYPE
+ *            otherwise.
+ *   lse      float32 [B, H, Nq], contiguous, as for mifa_attention.
+ * Other arguments as for mifa_attention.  Errors in the order NULL (strides too), shape, d,
+ * alignment of the pointers, scale, size, then o_dtype, then the strides.
+ */
+int mifa_attention_strided(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                           const int64_t* strides, int o_dtype, int causal, float scale,
+                           void* stream);
 
 /*
  * mifa_attention_splitkv -- mifa_attention with the keys of each head cut into ranges that
@@ -152,6 +177,25 @@ int mifa_bwd(const void* q, const void* k, const void* v, const float* o, const 
              const void* dO, float* dq, float* dk, float* dv, int64_t B, int64_t H, int64_t Nq,
              int64_t Nk, int64_t d, int causal, float scale, void* workspace,
              int64_t workspace_bytes, void* stream);
+
+/*
+ * mifa_bwd_strided -- mifa_bwd on tensors of any (batch, head, row) strides, with O read as
+ * float32 or bf16 and the gradients written as float32 or bf16 (what an autograd function over
+ * mifa_attention_strided needs: gradients in the inputs' layout and type, without copies).
+ *
+ *   strides     host array of 24 int64: the (batch, head, row) strides, in elements, of q, k,
+ *               v, o, dO, dq, dk, dv in that order; d is contiguous.  Rules as for
+ *               mifa_attention_strided (>= 0, multiples of 8, row strides below 2^24).
+ *   o_dtype     type of o: MIFA_DTYPE_F32 or MIFA_DTYPE_BF16.
+ *   grad_dtype  type of dq, dk, dv: MIFA_DTYPE_F32 or MIFA_DTYPE_BF16 (rounded to nearest even).
+ * Other arguments as for mifa_bwd.  Errors in the order NULL (strides too), shape, d, pointer
+ * alignment, scale, size, then the dtypes, then the strides, then the workspace.
+ */
+int mifa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dO, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                     int64_t Nq, int64_t Nk, int64_t d, const int64_t* strides, int o_dtype,
+                     int grad_dtype, int causal, float scale, void* workspace,
+                     int64_t workspace_bytes, void* stream);
 
 /* Workspace bytes mifa_bwd needs for this shape (0 for an invalid shape). */
 int64_t mifa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);

@@ -27,10 +27,12 @@ STATUS_NAMES = {
     7: "MIFA_ERR_HIP",
     8: "MIFA_ERR_BAD_DTYPE",
     9: "MIFA_ERR_WORKSPACE",
+    10: "MIFA_ERR_BAD_STRIDE",
 }
 MIFA_DTYPE_BF16, MIFA_DTYPE_F32 = 0, 1
-EXPORTED = ("mifa_fwd", "mifa_attention", "mifa_attention_splitkv", "mifa_splitkv_workspace_bytes",
-            "mifa_bwd", "mifa_bwd_workspace_bytes", "mifa_softmax_rows", "mifa_status_string", "mifa_version", "mifa_last_hip_error")
+EXPORTED = ("mifa_fwd", "mifa_attention", "mifa_attention_strided", "mifa_attention_splitkv",
+            "mifa_splitkv_workspace_bytes", "mifa_bwd", "mifa_bwd_strided", "mifa_bwd_workspace_bytes",
+            "mifa_softmax_rows", "mifa_status_string", "mifa_version", "mifa_last_hip_error")
 
 
 class MifaError(RuntimeError):
@@ -60,6 +62,14 @@ def _load() -> ctypes.CDLL:
     lib.mifa_bwd.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int64] * 5 +
                              [ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p])
     lib.mifa_bwd.restype = ctypes.c_int
+    lib.mifa_attention_strided.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 +
+                                           [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                            ctypes.c_void_p])
+    lib.mifa_attention_strided.restype = ctypes.c_int
+    lib.mifa_bwd_strided.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int64] * 5 +
+                                     [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                      ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p])
+    lib.mifa_bwd_strided.restype = ctypes.c_int
     lib.mifa_bwd_workspace_bytes.argtypes = [ctypes.c_int64] * 3
     lib.mifa_bwd_workspace_bytes.restype = ctypes.c_int64
     lib.mifa_softmax_rows.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_float,
@@ -139,6 +149,38 @@ def mifa_splitkv_workspace_bytes(B, H, Nq, Nk, d) -> int:
     return int(_lib.mifa_splitkv_workspace_bytes(int(B), int(H), int(Nq), int(Nk), int(d)))
 
 
+def _strides_array(strides):
+    """A host int64 array for the strides argument, or a plain integer address (tests)."""
+    if strides is None or isinstance(strides, int):
+        return strides or None
+    return (ctypes.c_int64 * len(strides))(*[int(x) for x in strides])
+
+
+def mifa_attention_strided_raw(q, k, v, o, lse, B, H, Nq, Nk, d, strides, o_dtype, causal, scale, stream) -> int:
+    """Call the C entry point; `strides`: 12 ints (batch, head, row strides of q, k, v, o)."""
+    return int(_lib.mifa_attention_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq),
+                                           int(Nk), int(d), _strides_array(strides), int(o_dtype),
+                                           1 if causal else 0, float(scale), stream or None))
+
+
+def mifa_bwd_strided_raw(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, d, strides, o_dtype, grad_dtype, causal,
+                         scale, workspace, workspace_bytes, stream) -> int:
+    """Call the C entry point; `strides`: 24 ints (q, k, v, o, dO, dq, dk, dv)."""
+    return int(_lib.mifa_bwd_strided(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(do), _ptr(dq), _ptr(dk),
+                                     _ptr(dv), int(B), int(H), int(Nq), int(Nk), int(d), _strides_array(strides),
+                                     int(o_dtype), int(grad_dtype), 1 if causal else 0, float(scale),
+                                     _ptr(workspace), int(workspace_bytes), stream or None))
+
+
+def _bhn(t):
+    """(batch, head, row) strides of a [B, H, N, d] tensor whose d is contiguous."""
+    return list(t.stride()[:3])
+
+
+def _dense_bhnd(t) -> bool:
+    return t.is_contiguous()
+
+
 def _check(name, t, shape=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -148,20 +190,23 @@ def _check(name, t, shape=None):
         raise ValueError(f"{name} must be bfloat16, got {t.dtype}")
     if t.dim() != 4:
         raise ValueError(f"{name} must be [B, H, N, d]")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    if t.dim() == 4 and t.shape[3] > 1 and t.stride(3) != 1:
+        raise ValueError(f"{name} must have its last (d) dimension contiguous")
     if shape is not None and tuple(t.shape) != shape:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
 
 
-def _outputs(q, out, lse):
+_MIFA_DTYPES = {torch.float32: 1, torch.bfloat16: 0}
+
+
+def _outputs(q, out, lse, out_dtype=torch.float32):
     B, H, Nq, d = q.shape
     if out is None:
-        out = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, H, Nq, d), dtype=out_dtype, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != torch.float32 or not out.is_contiguous() or out.device != q.device:
-        raise ValueError("out must be a contiguous float32 tensor shaped like q on q's device")
+    if out.shape != q.shape or out.dtype not in _MIFA_DTYPES or out.device != q.device or out.stride(3) != 1:
+        raise ValueError("out must be a float32 or bfloat16 tensor shaped like q on q's device, d contiguous")
     if lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
         raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
     return out, lse
@@ -181,22 +226,29 @@ def _qkv(q, k, v):
 
 
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, scale=None,
-              out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+              out: torch.Tensor | None = None, lse: torch.Tensor | None = None, out_dtype=torch.float32):
     """Exact attention forward.  q: bf16 [B, H, Nq, d], k, v: bf16 [B, H, Nk, d] on the GPU
-    (d = 64 or 128; causal needs Nq <= Nk, the queries being the last Nq positions).
+    (d = 64 or 128; causal needs Nq <= Nk, the queries being the last Nq positions).  Any
+    (batch, head, row) strides are read in place (d contiguous, strides multiples of 8).
 
-    Returns (O float32 [B, H, Nq, d], LSE float32 [B, H, Nq]); both are allocated here unless
-    given.  The launch is asynchronous on torch's current stream."""
+    Returns (O [B, H, Nq, d] of out_dtype -- float32 or bfloat16 --, LSE float32 [B, H, Nq]);
+    both are allocated here unless given (`out` may be strided too).  The launch is
+    asynchronous on torch's current stream."""
     B, H, Nq, Nk, d = _qkv(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    out, lse = _outputs(q, out, lse)
+    out, lse = _outputs(q, out, lse, out_dtype)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        if Nq == Nk:
-            mifa_fwd(q, k, v, out, lse, B, H, Nq, d, causal, scale, stream)
+        if all(_dense_bhnd(t) for t in (q, k, v, out)) and out.dtype == torch.float32:
+            if Nq == Nk:
+                mifa_fwd(q, k, v, out, lse, B, H, Nq, d, causal, scale, stream)
+            else:
+                _raise(mifa_attention_raw(q, k, v, out, lse, B, H, Nq, Nk, d, causal, scale, stream))
         else:
-            _raise(mifa_attention_raw(q, k, v, out, lse, B, H, Nq, Nk, d, causal, scale, stream))
+            strides = _bhn(q) + _bhn(k) + _bhn(v) + _bhn(out)
+            _raise(mifa_attention_strided_raw(q, k, v, out, lse, B, H, Nq, Nk, d, strides, _MIFA_DTYPES[out.dtype],
+                                              causal, scale, stream))
     return out, lse
 
 
@@ -204,12 +256,15 @@ def attention_splitkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal:
                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                       workspace: torch.Tensor | None = None):
     """attention() with each head's keys split into ranges processed in parallel and merged
-    by LSE (for few queries against many keys).  `workspace`: a GPU tensor of at least
-    mifa_splitkv_workspace_bytes(...) bytes, allocated here (uint8) unless given."""
+    by LSE (for few queries against many keys).  Contiguous tensors and float32 O only.
+    `workspace`: a GPU tensor of at least mifa_splitkv_workspace_bytes(...) bytes, allocated
+    here (uint8) unless given."""
     B, H, Nq, Nk, d = _qkv(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out, lse = _outputs(q, out, lse)
+    if not all(_dense_bhnd(t) for t in (q, k, v, out)) or out.dtype != torch.float32:
+        raise ValueError("the split-KV path takes contiguous q, k, v and a contiguous float32 out")
     need = mifa_splitkv_workspace_bytes(B, H, Nq, Nk, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
@@ -235,28 +290,46 @@ def mifa_bwd_workspace_bytes(B, H, Nq) -> int:
 
 
 def attention_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
-                       do: torch.Tensor, causal: bool = False, scale=None, workspace: torch.Tensor | None = None):
-    """Gradients (dq, dk, dv), float32 shaped like q, k, v, of attention(q, k, v, causal, scale)
-    for the upstream gradient do (bf16, shaped like q); o and lse are that forward's outputs.
-    `workspace`: a GPU tensor of at least mifa_bwd_workspace_bytes(B, H, Nq) bytes, allocated
-    here (uint8) unless given.  Asynchronous on torch's current stream."""
+                       do: torch.Tensor, causal: bool = False, scale=None, workspace: torch.Tensor | None = None,
+                       grad_dtype=torch.float32, grads=None):
+    """Gradients (dq, dk, dv) of attention(q, k, v, causal, scale) for the upstream gradient
+    do (bf16, shaped like q); o (float32 or bf16) and lse are that forward's outputs.  Any
+    (batch, head, row) strides are read in place (d contiguous).  The gradients are allocated
+    here, dense and of grad_dtype (float32 or bfloat16), unless `grads` = (dq, dk, dv) is
+    given (any strides, one of those two types).  `workspace`: a GPU tensor of at least
+    mifa_bwd_workspace_bytes(B, H, Nq) bytes, allocated here (uint8) unless given.
+    Asynchronous on torch's current stream."""
     B, H, Nq, Nk, d = _qkv(q, k, v)
     _check("do", do, (B, H, Nq, d))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    for name, t, shape in (("o", o, (B, H, Nq, d)), ("lse", lse, (B, H, Nq))):
-        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous() or t.device != q.device:
-            raise ValueError(f"{name} must be a contiguous float32 {shape} tensor on q's device")
-    dq = torch.empty((B, H, Nq, d), dtype=torch.float32, device=q.device)
-    dk = torch.empty((B, H, Nk, d), dtype=torch.float32, device=q.device)
-    dv = torch.empty((B, H, Nk, d), dtype=torch.float32, device=q.device)
+    if (tuple(o.shape) != (B, H, Nq, d) or o.dtype not in _MIFA_DTYPES or o.device != q.device
+            or o.stride(3) != 1):
+        raise ValueError("o must be a float32 or bfloat16 [B, H, Nq, d] tensor on q's device, d contiguous")
+    if tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32 or not lse.is_contiguous() or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
+    if grads is None:
+        grads = (torch.empty((B, H, Nq, d), dtype=grad_dtype, device=q.device),
+                 torch.empty((B, H, Nk, d), dtype=grad_dtype, device=q.device),
+                 torch.empty((B, H, Nk, d), dtype=grad_dtype, device=q.device))
+    dq, dk, dv = grads
+    for name, g, shape in (("dq", dq, (B, H, Nq, d)), ("dk", dk, (B, H, Nk, d)), ("dv", dv, (B, H, Nk, d))):
+        if tuple(g.shape) != shape or g.dtype != dq.dtype or g.dtype not in _MIFA_DTYPES or g.stride(3) != 1:
+            raise ValueError(f"{name} must be a {shape} tensor of one type (float32 or bfloat16), d contiguous")
     need = mifa_bwd_workspace_bytes(B, H, Nq)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     nbytes = workspace.numel() * workspace.element_size()
     with torch.cuda.device(q.device):
-        _raise(mifa_bwd_raw(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, d, causal, scale, workspace, nbytes,
-                            torch.cuda.current_stream(q.device).cuda_stream))
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        if all(_dense_bhnd(t) for t in (q, k, v, o, do, dq, dk, dv)) and o.dtype == dq.dtype == torch.float32:
+            _raise(mifa_bwd_raw(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, d, causal, scale, workspace, nbytes,
+                                stream))
+        else:
+            strides = sum((_bhn(t) for t in (q, k, v, o, do, dq, dk, dv)), [])
+            _raise(mifa_bwd_strided_raw(q, k, v, o, lse, do, dq, dk, dv, B, H, Nq, Nk, d, strides,
+                                        _MIFA_DTYPES[o.dtype], _MIFA_DTYPES[dq.dtype], causal, scale, workspace,
+                                        nbytes, stream))
     return dq, dk, dv
 
 

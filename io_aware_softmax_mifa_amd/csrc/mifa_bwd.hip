@@ -54,9 +54,10 @@ struct Geo {
 // ---- tiles in LDS --------------------------------------------------------------------------
 // A block of kBlk rows x D bf16, rows of D*2 bytes, 16-byte chunk c of row r at c ^ swz_k(r).
 // DMA instruction t of this wave covers rows (wave*kInstPerWave + t)*kRowsPerInst ...; rows past
-// row_limit are clamped to it (the last, partial block).
+// row_limit are clamped to it (the last, partial block).  Source rows are rsb bytes apart.
 template <int D>
-__device__ __forceinline__ void dma_tile(const __bf16* src, char* dst, int wave, int lane, int row_limit) {
+__device__ __forceinline__ void dma_tile(const __bf16* src, char* dst, int wave, int lane, int row_limit,
+                                         unsigned rsb) {
   using G = Geo<D>;
   const char* s = (const char*)src;
 #pragma unroll
@@ -65,7 +66,7 @@ __device__ __forceinline__ void dma_tile(const __bf16* src, char* dst, int wave,
     const int r = inst * G::kRowsPerInst + lane / G::kChunksPerRow;
     const int pc = lane % G::kChunksPerRow;
     const int rr = r < row_limit ? r : row_limit;
-    const unsigned off = (unsigned)(rr * (D * 2) + ((pc ^ swz_k<D>(r)) * 16));
+    const unsigned off = (unsigned)rr * rsb + (unsigned)((pc ^ swz_k<D>(r)) * 16);
     __builtin_amdgcn_global_load_lds((global_cvoid*)(s + off), (lds_void*)(dst + inst * 1024), 16, 0, 0);
   }
 }
@@ -97,14 +98,14 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Load 32 rows x D of a bf16 [rows, D] tensor into the B-operand layout of a 32x32x16 MFMA:
-// lane l holds row l%32, elements 16s + 8(l/32) .. +7 of slice s.  Rows at or past `rows`
-// are clamped; flip = 1 negates (sign bit) every element.
+// Load 32 rows x D of a bf16 tensor (rows rs elements apart) into the B-operand layout of a
+// 32x32x16 MFMA: lane l holds row l%32, elements 16s + 8(l/32) .. +7 of slice s.  Rows at or
+// past `rows` are clamped; flip = 1 negates (sign bit) every element.
 template <int D>
-__device__ __forceinline__ void load_rows(const __bf16* base, int row, int rows, int hf, int flip,
+__device__ __forceinline__ void load_rows(const __bf16* base, int64_t rs, int row, int rows, int hf, int flip,
                                           bf16x8 (&f)[D / 16]) {
   const int r = row < rows ? row : rows - 1;
-  const __bf16* src = base + (int64_t)r * D + 8 * hf;
+  const __bf16* src = base + r * rs + 8 * hf;
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     u32x4 raw = *(const u32x4*)(src + 16 * s);
@@ -124,17 +125,23 @@ __device__ __forceinline__ void pack(const f32x16 (&x)[2], bf16x8 (&pb)[4]) {
 }
 
 // Store a transposed accumulator (lane = output row, 16 values of a 32-column tile t) scaled by
-// `mul` to row `row` of a float [rows, D] tensor.
+// `mul` to the row at element offset `off` of a float32 (or, with as_bf16, bf16) tensor.
 template <int D>
-__device__ __forceinline__ void store_row(float* base, int row, int hf, const f32x16 (&acc)[D / 32], float mul) {
-  float* dst = base + (int64_t)row * D;
+__device__ __forceinline__ void store_row(void* base, int64_t off, int hf, const f32x16 (&acc)[D / 32], float mul,
+                                          int as_bf16) {
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const f32x4 v = {acc[t][4 * g4] * mul, acc[t][4 * g4 + 1] * mul, acc[t][4 * g4 + 2] * mul,
                        acc[t][4 * g4 + 3] * mul};
-      *(f32x4*)(dst + 32 * t + 8 * g4 + 4 * hf) = v;
+      const int64_t e = off + 32 * t + 8 * g4 + 4 * hf;
+      if (as_bf16) {
+        const __bf16 r[4] = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        *(uint64_t*)((__bf16*)base + e) = __builtin_bit_cast(uint64_t, r);
+      } else {
+        *(f32x4*)((float*)base + e) = v;
+      }
     }
 }
 
@@ -204,6 +211,11 @@ __device__ __forceinline__ void tr_addrs(unsigned tile, int lane, unsigned (&tra
 }
 
 // ---- launch parameters ------------------------------------------------------------------------
+// Element (b, h, i, t) of q sits at b q[0] + h q[1] + i q[2] + t (strides in elements); likewise
+// the other tensors.  LSE and D are [B*H, Nq], contiguous.
+struct Strides {
+  int64_t b, h, n;
+};
 struct BwdParams {
   const __bf16* q;
   const __bf16* k;
@@ -211,9 +223,11 @@ struct BwdParams {
   const __bf16* dO;
   const float* lse;   // forward LSE, [BH, Nq]
   const float* dd;    // D = rowsum(dO * O), [BH, Nq]
-  float* dq;
-  float* dk;
-  float* dv;
+  void* dq;
+  void* dk;
+  void* dv;
+  Strides sq, sk, sv, sdo, sdq, sdk, sdv;
+  int H, g_bf16;      // g_bf16: dq, dk, dv in bf16 (else float32)
   int Nq, Nk, BH;
   float c_log2;       // |scale| * log2(e)
   float scale;        // signed, for dQ and dK
@@ -221,18 +235,29 @@ struct BwdParams {
 };
 
 // ---- D = rowsum(dO * O) --------------------------------------------------------------------
+// O is float32, or bf16 when o_bf16 is set; row r of D is (b*H + h)*Nq + i.
 template <int D>
-__global__ __launch_bounds__(64) void row_dot_kernel(const __bf16* __restrict__ dO, const float* __restrict__ o,
-                                                     float* __restrict__ dd, int64_t rows) {
+__global__ __launch_bounds__(64) void row_dot_kernel(const __bf16* __restrict__ dO, Strides sdo,
+                                                     const void* __restrict__ o, Strides so, int o_bf16,
+                                                     float* __restrict__ dd, int H, int Nq, int64_t rows) {
   constexpr int TPR = D / 4, RPB = 64 / TPR;
   const int t = threadIdx.x % TPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
   float s = 0.f;
   if (row < rows) {
-    const f32x4 ov = *(const f32x4*)(o + row * D + 4 * t);
-    const uint64_t raw = *(const uint64_t*)(dO + row * D + 4 * t);
+    const int64_t bh = row / Nq, i = row - bh * Nq, b = bh / H, h = bh - b * H;
+    const int64_t oe = b * so.b + h * so.h + i * so.n + 4 * t;
+    f32x4 ov;
+    if (o_bf16) {
+      const uint64_t raw = *(const uint64_t*)((const __bf16*)o + oe);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s += __builtin_bit_cast(float, (unsigned)((raw >> (16 * i)) & 0xffffu) << 16) * ov[i];
+      for (int j = 0; j < 4; ++j) ov[j] = __builtin_bit_cast(float, (unsigned)((raw >> (16 * j)) & 0xffffu) << 16);
+    } else {
+      ov = *(const f32x4*)((const float*)o + oe);
+    }
+    const uint64_t raw = *(const uint64_t*)(dO + b * sdo.b + h * sdo.h + i * sdo.n + 4 * t);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += __builtin_bit_cast(float, (unsigned)((raw >> (16 * j)) & 0xffffu) << 16) * ov[j];
   }
 #pragma unroll
   for (int off = TPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, TPR);
@@ -249,12 +274,18 @@ void dq_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, ln = lane & 31, hf = lane >> 5;
   const int BH = p.BH, Nq = p.Nq, Nk = p.Nk, kshift = Nk - Nq;
-  const int bh = blockIdx.x % BH, qt = blockIdx.x / BH;
+  // Workgroup w runs on XCD w % 8, so with BH a multiple of 8 all tiles of a head share one
+  // XCD's L2.  Causal tiles go heaviest first: tiles that start together have about the same
+  // length and stream the same K/V blocks in step, which keeps those blocks in L2.
+  const int n_qt = (Nq + kRows - 1) / kRows;
+  const int bh = blockIdx.x % BH, rank = blockIdx.x / BH;
+  const int qt = CAUSAL ? n_qt - 1 - rank : rank;
   const int my_row = qt * kRows + wave * 32 + ln;
 
+  const int b = bh / p.H, h = bh - b * p.H;
   bf16x8 qf[G::kDS], dof[G::kDS];
-  load_rows<D>(p.q + (int64_t)bh * Nq * D, my_row, Nq, hf, p.negate, qf);
-  load_rows<D>(p.dO + (int64_t)bh * Nq * D, my_row, Nq, hf, 0, dof);
+  load_rows<D>(p.q + b * p.sq.b + h * p.sq.h, p.sq.n, my_row, Nq, hf, p.negate, qf);
+  load_rows<D>(p.dO + b * p.sdo.b + h * p.sdo.h, p.sdo.n, my_row, Nq, hf, 0, dof);
   const int rc = my_row < Nq ? my_row : Nq - 1;
   const float lse2 = p.lse[(int64_t)bh * Nq + rc] * 1.4426950408889634f;
   const float drow = p.dd[(int64_t)bh * Nq + rc];
@@ -269,25 +300,26 @@ void dq_kernel(BwdParams p) {
     nblk = min(n_kb, (last_row + kshift) / kBlk + 1);
     j_mask = min(j_mask, (qt * kRows + kshift) / kBlk);
   }
-  const __bf16* kh = p.k + (int64_t)bh * Nk * D;
-  const __bf16* vh = p.v + (int64_t)bh * Nk * D;
+  const __bf16* kh = p.k + b * p.sk.b + h * p.sk.h;
+  const __bf16* vh = p.v + b * p.sv.b + h * p.sv.h;
+  const unsigned ksb = (unsigned)(p.sk.n * 2), vsb = (unsigned)(p.sv.n * 2);
   const unsigned base = (unsigned)(uintptr_t)(lds_void*)smem;
   const int my_pos = my_row + kshift;
 
-  // Buffer b holds K at smem + 2b kTile and V at smem + (2b + 1) kTile.
-  dma_tile<D>(kh, smem, wave, lane, Nk - 1);
-  dma_tile<D>(vh, smem + G::kTile, wave, lane, Nk - 1);
+  // Buffer bf holds K at smem + 2 bf kTile and V at smem + (2 bf + 1) kTile.
+  dma_tile<D>(kh, smem, wave, lane, Nk - 1, ksb);
+  dma_tile<D>(vh, smem + G::kTile, wave, lane, Nk - 1, vsb);
   for (int j = 0; j < nblk; ++j) {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // block j has landed for every wave; block j-1 is done
-    const int b = j & 1;
+    const int bf = j & 1;
     if (j + 1 < nblk) {
       const int nb = (j + 1) & 1;
       const int limit = Nk - 1 - (j + 1) * kBlk;
-      dma_tile<D>(kh + (int64_t)(j + 1) * kBlk * D, smem + 2 * nb * G::kTile, wave, lane, limit);
-      dma_tile<D>(vh + (int64_t)(j + 1) * kBlk * D, smem + (2 * nb + 1) * G::kTile, wave, lane, limit);
+      dma_tile<D>(kh + (int64_t)(j + 1) * kBlk * p.sk.n, smem + 2 * nb * G::kTile, wave, lane, limit, ksb);
+      dma_tile<D>(vh + (int64_t)(j + 1) * kBlk * p.sv.n, smem + (2 * nb + 1) * G::kTile, wave, lane, limit, vsb);
     }
-    const unsigned kt_base = base + 2 * b * G::kTile, vt_base = kt_base + G::kTile;
+    const unsigned kt_base = base + 2 * bf * G::kTile, vt_base = kt_base + G::kTile;
     f32x16 s[2], dp[2];
     rowmajor_products<D>(kt_base, ln, hf, qf, s);
     rowmajor_products<D>(vt_base, ln, hf, dof, dp);
@@ -316,7 +348,8 @@ void dq_kernel(BwdParams p) {
     transposed_products<D>(tra, dsb, acc);
   }
   wait_vmcnt<0>();
-  if (my_row < Nq) store_row<D>(p.dq + (int64_t)bh * Nq * D, my_row, hf, acc, p.scale);
+  if (my_row < Nq)
+    store_row<D>(p.dq, b * p.sdq.b + h * p.sdq.h + my_row * p.sdq.n, hf, acc, p.scale, p.g_bf16);
 }
 
 // ---- dK, dV -------------------------------------------------------------------------------
@@ -365,13 +398,16 @@ void dkdv_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, ln = lane & 31, hf = lane >> 5;
   const int BH = p.BH, Nq = p.Nq, Nk = p.Nk, kshift = Nk - Nq;
+  // Key tile kb sees the query blocks from about kb on (causal), so ascending kb is already
+  // heaviest first; see dq_kernel for the XCD placement.
   const int bh = blockIdx.x % BH, kb = blockIdx.x / BH;
   const int tile_key0 = kb * kRows;
   const int my_key = tile_key0 + wave * 32 + ln;
 
+  const int b = bh / p.H, h = bh - b * p.H;
   bf16x8 kf[G::kDS], vf[G::kDS];
-  load_rows<D>(p.k + (int64_t)bh * Nk * D, my_key, Nk, hf, p.negate, kf);
-  load_rows<D>(p.v + (int64_t)bh * Nk * D, my_key, Nk, hf, 0, vf);
+  load_rows<D>(p.k + b * p.sk.b + h * p.sk.h, p.sk.n, my_key, Nk, hf, p.negate, kf);
+  load_rows<D>(p.v + b * p.sv.b + h * p.sv.h, p.sv.n, my_key, Nk, hf, 0, vf);
   f32x16 dv[G::kDT], dk[G::kDT];
 #pragma unroll
   for (int t = 0; t < G::kDT; ++t) dv[t] = dk[t] = (f32x16){};
@@ -382,8 +418,9 @@ void dkdv_kernel(BwdParams p) {
   const int n_qb = (Nq + kBlk - 1) / kBlk;
   int jb = 0;
   if (CAUSAL) jb = max(0, tile_key0 - kshift) / kBlk;
-  const __bf16* qh = p.q + (int64_t)bh * Nq * D;
-  const __bf16* doh = p.dO + (int64_t)bh * Nq * D;
+  const __bf16* qh = p.q + b * p.sq.b + h * p.sq.h;
+  const __bf16* doh = p.dO + b * p.sdo.b + h * p.sdo.h;
+  const unsigned qsb = (unsigned)(p.sq.n * 2), dosb = (unsigned)(p.sdo.n * 2);
   const float* lh = p.lse + (int64_t)bh * Nq;
   const float* dh = p.dd + (int64_t)bh * Nq;
   const unsigned base = (unsigned)(uintptr_t)(lds_void*)smem;
@@ -392,8 +429,8 @@ void dkdv_kernel(BwdParams p) {
   char* rowvals = smem + 4 * G::kTile;
   auto load_block = [&](int jq, int buf) {
     const int limit = Nq - 1 - jq * kBlk;
-    dma_tile<D>(qh + (int64_t)jq * kBlk * D, smem + 2 * buf * G::kTile, wave, lane, limit);
-    dma_tile<D>(doh + (int64_t)jq * kBlk * D, smem + (2 * buf + 1) * G::kTile, wave, lane, limit);
+    dma_tile<D>(qh + (int64_t)jq * kBlk * p.sq.n, smem + 2 * buf * G::kTile, wave, lane, limit, qsb);
+    dma_tile<D>(doh + (int64_t)jq * kBlk * p.sdo.n, smem + (2 * buf + 1) * G::kTile, wave, lane, limit, dosb);
     if (wave == 0) {
       const int r = lane < limit ? lane : limit;
       __builtin_amdgcn_global_load_lds((global_cvoid*)(lh + (int64_t)jq * kBlk + r), (lds_void*)(rowvals + buf * 512),
@@ -406,11 +443,11 @@ void dkdv_kernel(BwdParams p) {
   for (int jq = jb; jq < n_qb; ++jq) {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
-    const int b = (jq - jb) & 1;
-    if (jq + 1 < n_qb) load_block(jq + 1, b ^ 1);
-    const unsigned qt_base = base + 2 * b * G::kTile, dot_base = qt_base + G::kTile;
+    const int bf = (jq - jb) & 1;
+    if (jq + 1 < n_qb) load_block(jq + 1, bf ^ 1);
+    const unsigned qt_base = base + 2 * bf * G::kTile, dot_base = qt_base + G::kTile;
     // this lane's 16 query rows of tile tt: 32 tt + 8 g + 4 hf + (0..3), g = 0..3
-    const unsigned rv = base + 4 * G::kTile + b * 512;
+    const unsigned rv = base + 4 * G::kTile + bf * 512;
     const int q0 = jq * kBlk;
     const bool masked = (CAUSAL && q0 + kshift < tile_key0 + kRows - 1) || q0 + kBlk > Nq;
     unsigned tra_do[G::kDT][2], tra_q[G::kDT][2];
@@ -424,19 +461,20 @@ void dkdv_kernel(BwdParams p) {
   }
   wait_vmcnt<0>();
   if (my_key < Nk) {
-    store_row<D>(p.dv + (int64_t)bh * Nk * D, my_key, hf, dv, 1.f);
-    store_row<D>(p.dk + (int64_t)bh * Nk * D, my_key, hf, dk, p.scale);
+    store_row<D>(p.dv, b * p.sdv.b + h * p.sdv.h + my_key * p.sdv.n, hf, dv, 1.f, p.g_bf16);
+    store_row<D>(p.dk, b * p.sdk.b + h * p.sdk.h + my_key * p.sdk.n, hf, dk, p.scale, p.g_bf16);
   }
 }
 
 constexpr int kRowValsBytes = 2 * 512;
 
 template <int D, bool CAUSAL>
-hipError_t launch_bwd(const BwdParams& p, const float* o, float* dd, hipStream_t s) {
+hipError_t launch_bwd(const BwdParams& p, const void* o, Strides so, int o_bf16, float* dd, hipStream_t s) {
   using G = Geo<D>;
   const int64_t rows = (int64_t)p.BH * p.Nq;
   constexpr int rpb = 64 / (D / 4);
-  hipLaunchKernelGGL(row_dot_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(64), 0, s, p.dO, o, dd, rows);
+  hipLaunchKernelGGL(row_dot_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(64), 0, s, p.dO, p.sdo, o, so,
+                     o_bf16, dd, p.H, p.Nq, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static const hipError_t a1 =
@@ -463,9 +501,62 @@ extern "C" int64_t mifa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq) {
   return B * H * Nq * 4;
 }
 
-extern "C" int mifa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dO,
-                        float* dq, float* dk, float* dv, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
-                        int causal, float scale, void* workspace, int64_t workspace_bytes, void* stream) {
+namespace {
+
+// Argument checks and launch shared by both entry points.  st: (batch, head, row) strides in
+// elements of q, k, v, o, dO, dq, dk, dv.
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO, void* dq,
+            void* dk, void* dv, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, const int64_t* st,
+            int o_bf16, int g_bf16, int causal, float scale, void* workspace, int64_t workspace_bytes,
+            void* stream) {
+  const int64_t BH = B * H;
+  if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes < BH * Nq * 4) return MIFA_ERR_WORKSPACE;
+  BwdParams p;
+  p.q = (const __bf16*)q;
+  p.k = (const __bf16*)k;
+  p.v = (const __bf16*)v;
+  p.dO = (const __bf16*)dO;
+  p.lse = lse;
+  p.dd = (const float*)workspace;
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.sq = Strides{st[0], st[1], st[2]};
+  p.sk = Strides{st[3], st[4], st[5]};
+  p.sv = Strides{st[6], st[7], st[8]};
+  const Strides so{st[9], st[10], st[11]};
+  p.sdo = Strides{st[12], st[13], st[14]};
+  p.sdq = Strides{st[15], st[16], st[17]};
+  p.sdk = Strides{st[18], st[19], st[20]};
+  p.sdv = Strides{st[21], st[22], st[23]};
+  p.H = (int)H;
+  p.g_bf16 = g_bf16;
+  p.Nq = (int)Nq;
+  p.Nk = (int)Nk;
+  p.BH = (int)BH;
+  p.negate = scale < 0.f ? 1 : 0;
+  double c_exact = (double)(p.negate ? -scale : scale) * 1.4426950408889634;
+  if (c_exact < 1e-30) c_exact = 1e-30;
+  p.c_log2 = (float)c_exact;
+  p.scale = scale;
+  hipStream_t s = (hipStream_t)stream;
+  float* dd = (float*)workspace;
+  hipError_t e;
+  if (d == 128)
+    e = causal ? launch_bwd<128, true>(p, o, so, o_bf16, dd, s) : launch_bwd<128, false>(p, o, so, o_bf16, dd, s);
+  else
+    e = causal ? launch_bwd<64, true>(p, o, so, o_bf16, dd, s) : launch_bwd<64, false>(p, o, so, o_bf16, dd, s);
+  if (e != hipSuccess) {
+    mifa_record_hip_error((int)e);
+    return MIFA_ERR_HIP;
+  }
+  return MIFA_OK;
+}
+
+// The checks of mifa_bwd, in its documented order, up to (not including) the workspace.
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dO,
+              const void* dq, const void* dk, const void* dv, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+              int causal, float scale) {
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv) return MIFA_ERR_NULL_POINTER;
   if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (causal && Nq > Nk)) return MIFA_ERR_BAD_SHAPE;
   if (d != 64 && d != 128) return MIFA_ERR_UNSUPPORTED_D;
@@ -480,36 +571,49 @@ extern "C" int mifa_bwd(const void* q, const void* k, const void* v, const float
   if (BH >= ((int64_t)1 << 31) || BH * ((Nq + 127) / 128) >= ((int64_t)1 << 31) ||
       BH * ((Nk + 127) / 128) >= ((int64_t)1 << 31))
     return MIFA_ERR_TOO_LARGE;
-  if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes < BH * Nq * 4) return MIFA_ERR_WORKSPACE;
-
-  BwdParams p;
-  p.q = (const __bf16*)q;
-  p.k = (const __bf16*)k;
-  p.v = (const __bf16*)v;
-  p.dO = (const __bf16*)dO;
-  p.lse = lse;
-  p.dd = (const float*)workspace;
-  p.dq = dq;
-  p.dk = dk;
-  p.dv = dv;
-  p.Nq = (int)Nq;
-  p.Nk = (int)Nk;
-  p.BH = (int)BH;
-  p.negate = scale < 0.f ? 1 : 0;
-  double c_exact = (double)(p.negate ? -scale : scale) * 1.4426950408889634;
-  if (c_exact < 1e-30) c_exact = 1e-30;
-  p.c_log2 = (float)c_exact;
-  p.scale = scale;
-  hipStream_t s = (hipStream_t)stream;
-  float* dd = (float*)workspace;
-  hipError_t e;
-  if (d == 128)
-    e = causal ? launch_bwd<128, true>(p, o, dd, s) : launch_bwd<128, false>(p, o, dd, s);
-  else
-    e = causal ? launch_bwd<64, true>(p, o, dd, s) : launch_bwd<64, false>(p, o, dd, s);
-  if (e != hipSuccess) {
-    mifa_record_hip_error((int)e);
-    return MIFA_ERR_HIP;
-  }
   return MIFA_OK;
+}
+
+// The stride rules of the strided entry points, for n (batch, head, row) triples.
+int check_bwd_strides(const int64_t* st, int n) {
+  for (int i = 0; i < 3 * n; ++i)
+    if (st[i] < 0) return MIFA_ERR_BAD_STRIDE;
+  for (int i = 0; i < 3 * n; ++i)
+    if (st[i] % 8) return MIFA_ERR_MISALIGNED;
+  for (int i = 0; i < n; ++i)
+    if (st[3 * i + 2] >= ((int64_t)1 << 24)) return MIFA_ERR_TOO_LARGE;
+  return MIFA_OK;
+}
+
+}  // namespace
+
+extern "C" int mifa_bwd(const void* q, const void* k, const void* v, const float* o, const float* lse, const void* dO,
+                        float* dq, float* dk, float* dv, int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                        int causal, float scale, void* workspace, int64_t workspace_bytes, void* stream) {
+  const int st = check_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, causal, scale);
+  if (st != MIFA_OK) return st;
+  const int64_t sq[3] = {H * Nq * d, Nq * d, d}, sk[3] = {H * Nk * d, Nk * d, d};
+  int64_t strides[24];
+  // q, k, v, o, dO, dq, dk, dv
+  const int64_t* per[8] = {sq, sk, sk, sq, sq, sq, sk, sk};
+  for (int t = 0; t < 8; ++t)
+    for (int i = 0; i < 3; ++i) strides[3 * t + i] = per[t][i];
+  return run_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, strides, 0, 0, causal, scale, workspace,
+                 workspace_bytes, stream);
+}
+
+extern "C" int mifa_bwd_strided(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                const void* dO, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t Nq,
+                                int64_t Nk, int64_t d, const int64_t* strides, int o_dtype, int grad_dtype,
+                                int causal, float scale, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (!strides) return MIFA_ERR_NULL_POINTER;
+  int st = check_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, causal, scale);
+  if (st != MIFA_OK) return st;
+  if ((o_dtype != MIFA_DTYPE_BF16 && o_dtype != MIFA_DTYPE_F32) ||
+      (grad_dtype != MIFA_DTYPE_BF16 && grad_dtype != MIFA_DTYPE_F32))
+    return MIFA_ERR_BAD_DTYPE;
+  st = check_bwd_strides(strides, 8);
+  if (st != MIFA_OK) return st;
+  return run_bwd(q, k, v, o, lse, dO, dq, dk, dv, B, H, Nq, Nk, d, strides, o_dtype == MIFA_DTYPE_BF16 ? 1 : 0,
+                 grad_dtype == MIFA_DTYPE_BF16 ? 1 : 0, causal, scale, workspace, workspace_bytes, stream);
 }

@@ -109,13 +109,15 @@ struct Lane {
   unsigned v[C::kDT];           // V^T operand of dv tile t, key slice 0, V buffer 0
   unsigned dk[C::kInstPerWave]; // DMA source byte offsets within a key block (K)
   unsigned dv[C::kInstPerWave]; // (V)
+  unsigned ksb, vsb;            // K and V row strides in bytes (wave-uniform)
 };
 
 // DMA: instruction t of this wave covers rows inst*kRowsPerInst .. of the block; lane ->
 // (row, physical chunk); the source is the logical chunk that the swizzle places there.  Rows
 // past `row_limit` are clamped to it (only the last, partial block needs that).
 template <typename C>
-__device__ __forceinline__ void dma_offsets(unsigned* dk, unsigned* dv, int wave, int lane, int row_limit) {
+__device__ __forceinline__ void dma_offsets(unsigned* dk, unsigned* dv, int wave, int lane, int row_limit, unsigned ksb,
+                                            unsigned vsb) {
   constexpr int D = C::D;
 #pragma unroll
   for (int t = 0; t < C::kInstPerWave; ++t) {
@@ -123,13 +125,13 @@ __device__ __forceinline__ void dma_offsets(unsigned* dk, unsigned* dv, int wave
     const int r = inst * C::kRowsPerInst + lane / C::kChunksPerRow;
     const int pc = lane % C::kChunksPerRow;
     const int rr = r < row_limit ? r : row_limit;
-    dk[t] = (unsigned)(rr * (D * 2) + ((pc ^ swz_k<D>(r)) * 16));
-    dv[t] = (unsigned)(rr * (D * 2) + ((pc ^ swz_v<D>(r)) * 16));
+    dk[t] = (unsigned)rr * ksb + (unsigned)((pc ^ swz_k<D>(r)) * 16);
+    dv[t] = (unsigned)rr * vsb + (unsigned)((pc ^ swz_v<D>(r)) * 16);
   }
 }
 
 template <typename C>
-__device__ __forceinline__ Lane<C> lane_setup(unsigned smem_base, int wave, int lane) {
+__device__ __forceinline__ Lane<C> lane_setup(unsigned smem_base, int wave, int lane, unsigned ksb, unsigned vsb) {
   constexpr int D = C::D;
   Lane<C> a;
   const int ln = lane & 31, hf = lane >> 5;
@@ -143,7 +145,9 @@ __device__ __forceinline__ Lane<C> lane_setup(unsigned smem_base, int wave, int 
   const unsigned base = smem_base + C::kVBase + r * (D * 2) + (p & 1) * 8;
 #pragma unroll
   for (int t = 0; t < C::kDT; ++t) a.v[t] = base + (((4 * t + cl) ^ swz_v<D>(r)) * 16);
-  dma_offsets<C>(a.dk, a.dv, wave, lane, C::BC);
+  a.ksb = ksb;
+  a.vsb = vsb;
+  dma_offsets<C>(a.dk, a.dv, wave, lane, C::BC, ksb, vsb);
   return a;
 }
 
@@ -155,8 +159,8 @@ __device__ __forceinline__ void issue_dma(const __bf16* __restrict__ kbase, cons
                                           char* smem, int kblk, int kbuf, int vblk, int vbuf, int N, int wave,
                                           int lane, const Lane<C>& la) {
   constexpr int D = C::D, BC = C::BC;
-  const char* kb = (const char*)(kbase + (int64_t)kblk * BC * D);
-  const char* vb = (const char*)(vbase + (int64_t)vblk * BC * D);
+  const char* kb = (const char*)kbase + (int64_t)kblk * BC * la.ksb;
+  const char* vb = (const char*)vbase + (int64_t)vblk * BC * la.vsb;
   unsigned dk[C::kInstPerWave], dv[C::kInstPerWave], tk[C::kInstPerWave], tv[C::kInstPerWave];
 #pragma unroll
   for (int t = 0; t < C::kInstPerWave; ++t) {
@@ -166,10 +170,10 @@ __device__ __forceinline__ void issue_dma(const __bf16* __restrict__ kbase, cons
   // In the last, partial block, rows past N are clamped to N-1: they are masked out of the
   // softmax, and clamping keeps every global address inside the tensors.
   if (kblk * BC + BC > N) {
-    dma_offsets<C>(dk, tv, wave, lane, N - 1 - kblk * BC);
+    dma_offsets<C>(dk, tv, wave, lane, N - 1 - kblk * BC, la.ksb, la.vsb);
   }
   if (vblk * BC + BC > N) {
-    dma_offsets<C>(tk, dv, wave, lane, N - 1 - vblk * BC);
+    dma_offsets<C>(tk, dv, wave, lane, N - 1 - vblk * BC, la.ksb, la.vsb);
   }
   char* kdst = smem + kbuf * C::kTensorBytes;
   char* vdst = smem + C::kVBase + vbuf * C::kTensorBytes;
@@ -361,18 +365,32 @@ struct Wave {
   }
 };
 
+// Four consecutive O elements at element offset off: float32, or bf16 (round to nearest even).
+__device__ __forceinline__ void store_o4(void* o, int64_t off, f32x4 v, int as_bf16) {
+  if (as_bf16) {
+    const __bf16 r[4] = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *(uint64_t*)((__bf16*)o + off) = __builtin_bit_cast(uint64_t, r);
+  } else {
+    *(f32x4*)((float*)o + off) = v;
+  }
+}
+
 // Launch parameters.  Nq query rows and Nk keys per head; query i sits at position
 // i + Nk - Nq (so with Nq < Nk the queries are the newest positions, and the causal mask keeps
 // key j iff j <= i + Nk - Nq).  With n_splits > 1 the keys are cut into ranges of split_blocks
 // key blocks and split s writes the attention over its range alone (O normalised over that
 // range, LSE of that range; O = 0 and LSE = -inf where the range holds no visible key) to
-// o + s o_split and lse + s lse_split.
+// o + s o_split and lse + s lse_split.  Element (b, h, i, t) of q sits at
+// b q_sb + h q_sh + i q_sn + t (strides in elements; likewise k, v, o); LSE is [B*H, Nq].
+// O is float32, or bf16 when o_bf16 is set.
 struct FwdParams {
   const __bf16* q;
   const __bf16* k;
   const __bf16* v;
-  float* o;
+  void* o;
   float* lse;
+  int64_t q_sb, q_sh, q_sn, k_sb, k_sh, k_sn, v_sb, v_sh, v_sn, o_sb, o_sh, o_sn;
+  int H, o_bf16;
   int Nq, Nk, BH, n_qtiles;
   float c_log2;
   int negate_q, xcd_group;
@@ -432,10 +450,11 @@ void mifa_fwd_kernel(FwdParams p) {
   const int j_mask = j_mask_all - jb0;
   const int key_base = jb0 * BC;
 
-  const __bf16* __restrict__ qh = p.q + (int64_t)bh * Nq * D;
-  const __bf16* __restrict__ kh = p.k + ((int64_t)bh * Nk + key_base) * D;
-  const __bf16* __restrict__ vh = p.v + ((int64_t)bh * Nk + key_base) * D;
-  float* __restrict__ o_out = p.o + split * p.o_split + (int64_t)bh * Nq * D;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const __bf16* __restrict__ qh = p.q + b * p.q_sb + h * p.q_sh;
+  const __bf16* __restrict__ kh = p.k + b * p.k_sb + h * p.k_sh + key_base * p.k_sn;
+  const __bf16* __restrict__ vh = p.v + b * p.v_sb + h * p.v_sh + key_base * p.v_sn;
+  const int64_t o_off = split * p.o_split + b * p.o_sb + h * p.o_sh;
   float* __restrict__ lse_out = p.lse + split * p.lse_split + (int64_t)bh * Nq;
 
   Wave<C, CAUSAL> W;
@@ -454,7 +473,7 @@ void mifa_fwd_kernel(FwdParams p) {
   // ---- Q rows into VGPRs (B operand of S^T = K Q^T: lane holds q[row][16s + 8hf .. +7]) ----
   {
     const int r = W.my_row < Nq ? W.my_row : Nq - 1;
-    const __bf16* src = qh + (int64_t)r * D + 8 * hf;
+    const __bf16* src = qh + r * p.q_sn + 8 * hf;
 #pragma unroll
     for (int s = 0; s < C::kDS; ++s) {
       u32x4 raw = *(const u32x4*)(src + 16 * s);
@@ -467,17 +486,18 @@ void mifa_fwd_kernel(FwdParams p) {
   // writes its part: no weight (O = 0, LSE = -inf).  The test is uniform over the workgroup.
   if (nblk <= 0) {
     if (W.my_row < Nq) {
+      const int64_t orow = o_off + W.my_row * p.o_sn;
 #pragma unroll
       for (int t = 0; t < C::kDT; ++t)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) *(f32x4*)(o_out + (int64_t)W.my_row * D + 32 * t + 8 * g4 + 4 * hf) = (f32x4){};
+        for (int g4 = 0; g4 < 4; ++g4) store_o4(p.o, orow + 32 * t + 8 * g4 + 4 * hf, (f32x4){}, p.o_bf16);
       if (hf == 0) lse_out[W.my_row] = -__builtin_inff();
     }
     return;
   }
 
   const unsigned smem_base = (unsigned)(uintptr_t)(lds_void*)smem;
-  W.la = lane_setup<C>(smem_base, wave, lane);
+  W.la = lane_setup<C>(smem_base, wave, lane, (unsigned)(p.k_sn * 2), (unsigned)(p.v_sn * 2));
   // The two waves that share a SIMD run the same blocks between the same barriers.  A static
   // priority for the first half of the waves lets one of them run ahead, so that its MFMA-only
   // stretches (PV) line up with the other's VALU-heavy ones (softmax).
@@ -558,14 +578,14 @@ void mifa_fwd_kernel(FwdParams p) {
   const float l_tot = half_sum(W.l_run);
   if (W.my_row < Nq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* orow = o_out + (int64_t)W.my_row * D;
+    const int64_t orow = o_off + W.my_row * p.o_sn;
 #pragma unroll
     for (int t = 0; t < C::kDT; ++t)
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         f32x4 val = {W.oacc[t][4 * g4] * inv, W.oacc[t][4 * g4 + 1] * inv, W.oacc[t][4 * g4 + 2] * inv,
                      W.oacc[t][4 * g4 + 3] * inv};
-        *(f32x4*)(orow + 32 * t + 8 * g4 + 4 * hf) = val;
+        store_o4(p.o, orow + 32 * t + 8 * g4 + 4 * hf, val, p.o_bf16);
       }
     if (hf == 0) lse_out[W.my_row] = (W.m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994531f;
   }
@@ -574,11 +594,14 @@ void mifa_fwd_kernel(FwdParams p) {
 // Shape of one launch on the host side.
 struct Problem {
   const void *q, *k, *v;
-  float *o, *lse;
+  void* o;
+  float* lse;
   int Nq, Nk, BH;
   float scale;
   int n_splits, split_blocks;
   int64_t o_split, lse_split;
+  int H, o_bf16;
+  int64_t st[12];  // q, k, v, o: (batch, head, row) strides in elements
 };
 
 template <typename C, bool CAUSAL>
@@ -589,6 +612,12 @@ hipError_t launch(const Problem& pr, hipStream_t stream) {
   p.v = (const __bf16*)pr.v;
   p.o = pr.o;
   p.lse = pr.lse;
+  p.q_sb = pr.st[0], p.q_sh = pr.st[1], p.q_sn = pr.st[2];
+  p.k_sb = pr.st[3], p.k_sh = pr.st[4], p.k_sn = pr.st[5];
+  p.v_sb = pr.st[6], p.v_sh = pr.st[7], p.v_sn = pr.st[8];
+  p.o_sb = pr.st[9], p.o_sh = pr.st[10], p.o_sn = pr.st[11];
+  p.H = pr.H;
+  p.o_bf16 = pr.o_bf16;
   p.Nq = pr.Nq;
   p.Nk = pr.Nk;
   p.BH = pr.BH;
@@ -704,6 +733,30 @@ int check_attention(const void* q, const void* k, const void* v, const float* o,
   return MIFA_OK;
 }
 
+// Strides of dense [B, H, N, d] tensors: q and o with Nq rows, k and v with Nk rows.
+void dense_strides(int64_t H, int64_t Nq, int64_t Nk, int64_t d, int64_t* st) {
+  const int64_t sq[3] = {H * Nq * d, Nq * d, d}, sk[3] = {H * Nk * d, Nk * d, d};
+  for (int i = 0; i < 3; ++i) {
+    st[i] = sq[i];
+    st[3 + i] = sk[i];
+    st[6 + i] = sk[i];
+    st[9 + i] = sq[i];
+  }
+}
+
+// Stride checks for n (batch, head, row) triples, in elements: none negative, every one a
+// multiple of 8 elements (16-byte rows for bf16, the unit of the kernels' vector loads), and
+// row strides below 2^24 elements (per-lane offsets inside a 64-row block are 32-bit).
+int check_strides(const int64_t* st, int n) {
+  for (int i = 0; i < 3 * n; ++i)
+    if (st[i] < 0) return MIFA_ERR_BAD_STRIDE;
+  for (int i = 0; i < 3 * n; ++i)
+    if (st[i] % 8) return MIFA_ERR_MISALIGNED;
+  for (int i = 0; i < n; ++i)
+    if (st[3 * i + 2] >= ((int64_t)1 << 24)) return MIFA_ERR_TOO_LARGE;
+  return MIFA_OK;
+}
+
 thread_local int g_last_hip_error = 0;
 
 }  // namespace
@@ -714,7 +767,28 @@ int mifa_attention(const void* q, const void* k, const void* v, float* o, float*
                    int64_t Nq, int64_t Nk, int64_t d, int causal, float scale, void* stream) {
   const int st = check_attention(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale);
   if (st != MIFA_OK) return st;
-  const Problem pr{q, k, v, o, lse, (int)Nq, (int)Nk, (int)(B * H), scale, 1, 1 << 30, 0, 0};
+  Problem pr{q, k, v, o, lse, (int)Nq, (int)Nk, (int)(B * H), scale, 1, 1 << 30, 0, 0, (int)H, 0, {}};
+  dense_strides(H, Nq, Nk, d, pr.st);
+  const hipError_t e = dispatch_d(pr, (int)d, causal != 0, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return MIFA_ERR_HIP;
+  }
+  return MIFA_OK;
+}
+
+int mifa_attention_strided(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                           int64_t Nq, int64_t Nk, int64_t d, const int64_t* strides, int o_dtype, int causal,
+                           float scale, void* stream) {
+  if (!strides) return MIFA_ERR_NULL_POINTER;
+  int st = check_attention(q, k, v, (const float*)o, lse, B, H, Nq, Nk, d, causal, scale);
+  if (st != MIFA_OK) return st;
+  if (o_dtype != MIFA_DTYPE_BF16 && o_dtype != MIFA_DTYPE_F32) return MIFA_ERR_BAD_DTYPE;
+  st = check_strides(strides, 4);
+  if (st != MIFA_OK) return st;
+  Problem pr{q, k, v, o, lse, (int)Nq, (int)Nk, (int)(B * H), scale, 1, 1 << 30, 0, 0, (int)H,
+             o_dtype == MIFA_DTYPE_BF16 ? 1 : 0, {}};
+  for (int i = 0; i < 12; ++i) pr.st[i] = strides[i];
   const hipError_t e = dispatch_d(pr, (int)d, causal != 0, (hipStream_t)stream);
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
@@ -748,13 +822,15 @@ int mifa_attention_splitkv(const void* q, const void* k, const void* v, float* o
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (sp.n_splits == 1) {
-    const Problem pr{q, k, v, o, lse, (int)Nq, (int)Nk, (int)BH, scale, 1, sp.split_blocks, 0, 0};
+    Problem pr{q, k, v, o, lse, (int)Nq, (int)Nk, (int)BH, scale, 1, sp.split_blocks, 0, 0, (int)H, 0, {}};
+    dense_strides(H, Nq, Nk, d, pr.st);
     e = dispatch_d(pr, (int)d, causal != 0, s);
   } else {
     float* o_part = (float*)workspace;
     float* lse_part = o_part + (int64_t)sp.n_splits * BH * Nq * d;
-    const Problem pr{q, k, v, o_part, lse_part, (int)Nq, (int)Nk, (int)BH, scale, sp.n_splits, sp.split_blocks,
-                     BH * Nq * d, BH * Nq};
+    Problem pr{q,          k,  v,  o_part, lse_part, (int)Nq, (int)Nk, (int)BH, scale, sp.n_splits, sp.split_blocks,
+               BH * Nq * d, BH * Nq, (int)H, 0, {}};
+    dense_strides(H, Nq, Nk, d, pr.st);
     e = dispatch_d(pr, (int)d, causal != 0, s);
     if (e == hipSuccess) {
       const int64_t rows = BH * Nq;
@@ -782,12 +858,13 @@ const char* mifa_status_string(int status) {
     case MIFA_ERR_NULL_POINTER: return "null pointer argument";
     case MIFA_ERR_BAD_SHAPE: return "B, H, N (Nq, Nk) must be >= 1, and causal needs Nq <= Nk";
     case MIFA_ERR_UNSUPPORTED_D: return "head dimension d must be 64 or 128";
-    case MIFA_ERR_MISALIGNED: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case MIFA_ERR_MISALIGNED: return "tensors must be 16-byte aligned (lse 4-byte) and strides multiples of 8 elements";
     case MIFA_ERR_BAD_SCALE: return "scale must be finite";
     case MIFA_ERR_TOO_LARGE: return "problem too large (N*d or the tile count reaches 2^31)";
     case MIFA_ERR_HIP: return "HIP runtime error (see mifa_last_hip_error)";
     case MIFA_ERR_BAD_DTYPE: return "dtype must be MIFA_DTYPE_BF16 or MIFA_DTYPE_F32";
-    case MIFA_ERR_WORKSPACE: return "workspace NULL, not 16-byte aligned, or smaller than mifa_splitkv_workspace_bytes";
+    case MIFA_ERR_WORKSPACE: return "workspace NULL, not 16-byte aligned, or smaller than the entry point's *_workspace_bytes";
+    case MIFA_ERR_BAD_STRIDE: return "a stride is negative";
     default: return "unknown status";
   }
 }

@@ -21,9 +21,10 @@ def declared_functions():
 
 
 def test_header_declares_expected_api():
-    assert declared_functions() == ["mifa_attention", "mifa_attention_splitkv", "mifa_bwd", "mifa_bwd_workspace_bytes",
-                                    "mifa_fwd", "mifa_last_hip_error", "mifa_softmax_rows",
-                                    "mifa_splitkv_workspace_bytes", "mifa_status_string", "mifa_version"]
+    assert declared_functions() == ["mifa_attention", "mifa_attention_splitkv", "mifa_attention_strided", "mifa_bwd",
+                                    "mifa_bwd_strided", "mifa_bwd_workspace_bytes", "mifa_fwd",
+                                    "mifa_last_hip_error", "mifa_softmax_rows", "mifa_splitkv_workspace_bytes",
+                                    "mifa_status_string", "mifa_version"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -43,7 +44,7 @@ def lib():
 def test_version_and_status_strings(lib):
     assert lib.mifa_version().startswith("mifa ")
     assert "gfx950" in lib.mifa_version()
-    for code in range(10):
+    for code in range(11):
         s = lib.mifa_status_string(code)
         assert s and s != "unknown status"
     assert lib.mifa_status_string(99) == "unknown status"
@@ -228,3 +229,83 @@ def test_bwd_validation_order(lib):
 def test_bwd_workspace_bytes(lib):
     assert lib.mifa_bwd_workspace_bytes(0, 1, 1) == 0
     assert lib.mifa_bwd_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 4
+
+
+# ---- the strided entry points ----------------------------------------------------------------
+
+def _dense(H, Nq, Nk, d):
+    sq, sk = [H * Nq * d, Nq * d, d], [H * Nk * d, Nk * d, d]
+    return sq, sk
+
+
+def _fwd_strided(lib, strides="dense", o_dtype=1, q=A, Nq=100, Nk=100, d=128, causal=1, scale=0.1):
+    if strides == "dense":
+        sq, sk = _dense(2, Nq, Nk, d)
+        strides = sq + sk + sk + sq
+    return lib.mifa_attention_strided_raw(q, A, A, A, A, 1, 2, Nq, Nk, d, strides, o_dtype, causal, scale, None)
+
+
+def test_attention_strided_validation(lib):
+    sq, sk = _dense(2, 100, 100, 128)
+    assert _fwd_strided(lib, strides=None) == 1                  # NULL strides
+    assert _fwd_strided(lib, q=0) == 1
+    assert _fwd_strided(lib, Nq=101) == 2                        # causal needs Nq <= Nk
+    assert _fwd_strided(lib, d=96) == 3
+    assert _fwd_strided(lib, q=A + 8) == 4
+    assert _fwd_strided(lib, scale=float("nan")) == 5
+    assert _fwd_strided(lib, o_dtype=7) == 8
+    bad = sq + sk + sk + sq
+    bad[4] = -128                                                # negative head stride of k
+    assert _fwd_strided(lib, strides=bad) == 10
+    bad = sq + sk + sk + sq
+    bad[2] = 132                                                 # row stride not a multiple of 8
+    assert _fwd_strided(lib, strides=bad) == 4
+    bad = sq + sk + sk + sq
+    bad[5] = 1 << 24                                             # row stride too large
+    assert _fwd_strided(lib, strides=bad) == 6
+    # order: dtype before strides, strides after the scale
+    assert _fwd_strided(lib, o_dtype=7, strides=[-8] * 12) == 8
+    assert _fwd_strided(lib, scale=float("inf"), strides=[-8] * 12) == 5
+
+
+def _bwd_strided(lib, strides="dense", o_dtype=1, g_dtype=1, ws=A, wsb=1 << 40, dq=A, Nq=100, causal=1):
+    if strides == "dense":
+        sq, sk = _dense(2, Nq, 100, 128)
+        strides = sq + sk + sk + sq + sq + sq + sk + sk
+    return lib.mifa_bwd_strided_raw(A, A, A, A, A, A, dq, A, A, 1, 2, Nq, 100, 128, strides, o_dtype, g_dtype,
+                                    causal, 0.1, ws, wsb, None)
+
+
+def test_bwd_strided_validation(lib):
+    sq, sk = _dense(2, 100, 100, 128)
+    dense = sq + sk + sk + sq + sq + sq + sk + sk
+    assert _bwd_strided(lib, strides=None) == 1
+    assert _bwd_strided(lib, dq=0) == 1
+    assert _bwd_strided(lib, Nq=101) == 2
+    assert _bwd_strided(lib, o_dtype=5) == 8
+    assert _bwd_strided(lib, g_dtype=-1) == 8
+    bad = list(dense)
+    bad[13] = -8                                                 # dO head stride
+    assert _bwd_strided(lib, strides=bad) == 10
+    bad = list(dense)
+    bad[23] = 4                                                  # dv row stride
+    assert _bwd_strided(lib, strides=bad) == 4
+    assert _bwd_strided(lib, ws=0) == 9
+    assert _bwd_strided(lib, ws=0, strides=bad) == 4             # strides before the workspace
+
+
+def test_sdpa_argument_checks_need_no_gpu(lib):
+    import torch
+    from torch.nn.attention.bias import causal_upper_left
+
+    from io_aware_softmax_mifa_amd.sdpa import scaled_dot_product_attention as sdpa
+
+    x = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        sdpa(x, x, x)                                   # CPU tensors
+    with pytest.raises(ValueError):
+        sdpa(x.float(), x, x)
+    with pytest.raises(ValueError):
+        sdpa(x[0], x, x)                                # not 4-D
+    assert torch.ops.mifa.attention_fwd is not None and torch.ops.mifa.attention_bwd is not None
+    assert causal_upper_left(8, 8) is not None

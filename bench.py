@@ -400,6 +400,8 @@ def bench_backward(args):
     call_ms = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {call_ms:.4f} ms/call (HIP events; "
         "row_dot + dq + dkdv kernels)")
+    if args.copy_calibration:
+        copy_calibration(dev)
     f = bwd_flops(w)
     value = f / (ms_per_step * 1e-3) / 1e12
     achieved = f / (call_ms * 1e-3) / 1e12

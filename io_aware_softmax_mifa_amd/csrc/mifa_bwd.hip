@@ -52,7 +52,19 @@ struct Geo {
 };
 
 // ---- tiles in LDS --------------------------------------------------------------------------
-// A block of kBlk rows x D bf16, rows of D*2 bytes, 16-byte chunk c of row r at c ^ swz_k(r).
+// Every tile here is read both row-major (16 bytes of one row per lane: 16 lanes, 16 rows, per
+// LDS cycle) and transposed (8 bytes per lane: 32 lanes, 4 rows x 4 chunks, per cycle).  The XOR
+// swizzle of the 16-byte chunk index puts each cycle's accesses in distinct bank groups for both
+// patterns (64 banks of 4 bytes; measured on MI355X with SQ_LDS_BANK_CONFLICT: zero conflict
+// cycles for both).  d = 128 (256-byte rows): ((r & 3) << 2) | ((r >> 2) & 3).  d = 64 (two rows
+// per bank row): (((r >> 1) & 1) << 2) | ((r >> 2) & 3).  Both depend on r mod 16 only and stay
+// inside the row.
+template <int D>
+__device__ __forceinline__ int swz_b(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// A block of kBlk rows x D bf16, rows of D*2 bytes, 16-byte chunk c of row r at c ^ swz_b<D>(r).
 // DMA instruction t of this wave covers rows (wave*kInstPerWave + t)*kRowsPerInst ...; rows past
 // row_limit are clamped to it (the last, partial block).  Source rows are rsb bytes apart.
 template <int D>
@@ -66,7 +78,7 @@ __device__ __forceinline__ void dma_tile(const __bf16* src, char* dst, int wave,
     const int r = inst * G::kRowsPerInst + lane / G::kChunksPerRow;
     const int pc = lane % G::kChunksPerRow;
     const int rr = r < row_limit ? r : row_limit;
-    const unsigned off = (unsigned)rr * rsb + (unsigned)((pc ^ swz_k<D>(r)) * 16);
+    const unsigned off = (unsigned)rr * rsb + (unsigned)((pc ^ swz_b<D>(r)) * 16);
     __builtin_amdgcn_global_load_lds((global_cvoid*)(s + off), (lds_void*)(dst + inst * 1024), 16, 0, 0);
   }
 }
@@ -80,7 +92,7 @@ constexpr int dma_ops() {
 // applied here.
 template <int D>
 __device__ __forceinline__ unsigned row_addr(unsigned tile, int row, int s, int hf) {
-  return tile + row * (D * 2) + ((((2 * s + hf) ^ swz_k<D>(row))) * 16);
+  return tile + row * (D * 2) + ((((2 * s + hf) ^ swz_b<D>(row))) * 16);
 }
 
 // Transposing operand read (A operand of X^T Y): lane (g = lane/16, p = lane%16) reads, for
@@ -91,7 +103,7 @@ __device__ __forceinline__ unsigned tr_addr(unsigned tile, int lane, int t, int 
   const int g = lane >> 4, p = lane & 15, hf = lane >> 5;
   const int r = 4 * hf + (p >> 2) + 8 * hi;
   const int cl = 2 * (g & 1) + ((p & 3) >> 1);
-  return tile + r * (D * 2) + (p & 1) * 8 + (((4 * t + cl) ^ swz_k<D>(r)) * 16);
+  return tile + r * (D * 2) + (p & 1) * 8 + (((4 * t + cl) ^ swz_b<D>(r)) * 16);
 }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -353,6 +365,66 @@ void dq_kernel(BwdParams p) {
 }
 
 // ---- dK, dV -------------------------------------------------------------------------------
+// At one wave per SIMD nothing else hides an LDS round trip, so the reads of each stage are
+// issued ahead of the MFMAs of the stage before: the row values (LSE, D) and the Q and dO rows
+// of a tile go out together, and the transposed operands of the four dV/dK steps run one step
+// ahead.  Waits count the reads issued after the one needed (LDS reads complete in order);
+// counts above the 4-bit field are clamped, which only waits longer.
+template <int N>
+constexpr int kClampLgkm = N < 15 ? N : 15;
+
+template <int D>
+__device__ __forceinline__ void issue_rows(unsigned tile, int row, int hf, bf16x8 (&a)[D / 16]) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) a[s] = lds_read_b128<0>(row_addr<D>(tile, row, s, hf));
+}
+// acc = sum_s a[s] (x) f[s]; AFTER reads were issued after a[] (their order is a, then those).
+template <int D, int AFTER, int S>
+__device__ __forceinline__ void rows_mfma(bf16x8 (&a)[D / 16], const bf16x8 (&f)[D / 16], f32x16& acc, IC<S>) {
+  lgkm_wait<kClampLgkm<AFTER + D / 16 - 1 - S>>(a[S]);
+  acc = mfma(a[S], f[S], S == 0 ? (f32x16){} : acc);
+}
+template <int D, int AFTER>
+__device__ __forceinline__ void rows_product(bf16x8 (&a)[D / 16], const bf16x8 (&f)[D / 16], f32x16& acc) {
+  [&]<int... S>(std::integer_sequence<int, S...>) { (rows_mfma<D, AFTER>(a, f, acc, IC<S>{}), ...); }(
+      std::make_integer_sequence<int, D / 16>{});
+}
+
+// Transposed operand reads of contraction slice KS for every d tile (2 per tile).
+template <int D, int KS>
+struct TrReads {
+  i16x4 lo[D / 32], hi[D / 32];
+  __device__ __forceinline__ void issue(const unsigned (&tra)[D / 32][2]) {
+    constexpr int off = KS * 16 * D * 2;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) {
+      lo[t] = lds_read_tr<off>(tra[t][0]);
+      hi[t] = lds_read_tr<off>(tra[t][1]);
+    }
+  }
+  // acc[t] += tile^T slice KS (x) pb; AFTER reads were issued after these.
+  template <int AFTER>
+  __device__ __forceinline__ void mfmas(const bf16x8& pb, f32x16 (&acc)[D / 32]) {
+    [&]<int... T>(std::integer_sequence<int, T...>) {
+      ((lgkm_wait<kClampLgkm<AFTER + 2 * (D / 32 - 1 - T)>>(lo[T], hi[T]),
+        acc[T] = mfma(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[T], hi[T], 0, 1, 2, 3, 4, 5, 6, 7)), pb,
+                      acc[T])),
+       ...);
+    }(std::make_integer_sequence<int, D / 32>{});
+  }
+};
+
+__device__ __forceinline__ f32x4 lds_read_f32x4_at(unsigned addr) {
+  f32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+__device__ __forceinline__ f32x4 lds_read_f32x4_at256(unsigned addr) {
+  f32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:256" : "=v"(r) : "v"(addr));
+  return r;
+}
+
 // One 32-query tile TT of a query block: S = Q K^T and dP = dO V^T for the wave's 32 keys, then
 // P and dS, then dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries.
 template <int D, bool CAUSAL, int TT>
@@ -361,16 +433,26 @@ __device__ __forceinline__ void block_tile(unsigned qt_base, unsigned dot_base, 
                                            int Nq, int my_key, int kshift, float c_log2,
                                            const unsigned (&tra_do)[D / 32][2], const unsigned (&tra_q)[D / 32][2],
                                            f32x16 (&dv)[D / 32], f32x16 (&dk)[D / 32]) {
-  f32x16 s, dp;
-  rowmajor_tile<D>(qt_base, 32 * TT + ln, hf, kf, s);
-  rowmajor_tile<D>(dot_base, 32 * TT + ln, hf, vf, dp);
+  constexpr int kDS = D / 16, kTrPerStep = 2 * (D / 32);
+  // this lane's 16 query rows of the tile: 32 TT + 8 g + 4 hf + (0..3), g = 0..3
   f32x4 lv[4], dvv[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
     const unsigned ra = rv + (32 * TT + 8 * g + 4 * hf) * 4;
-    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:256\n\ts_waitcnt lgkmcnt(0)"
-                 : "=v"(lv[g]), "=v"(dvv[g]) : "v"(ra));
+    lv[g] = lds_read_f32x4_at(ra);
+    dvv[g] = lds_read_f32x4_at256(ra);
   }
+  bf16x8 qa[kDS], oa[kDS];
+  issue_rows<D>(qt_base, 32 * TT + ln, hf, qa);
+  issue_rows<D>(dot_base, 32 * TT + ln, hf, oa);
+  f32x16 s, dp;
+  rows_product<D, kDS>(qa, kf, s);
+  rows_product<D, 0>(oa, vf, dp);
+  // every read issued so far has landed (the last wait above counted none outstanding)
+#pragma unroll
+  for (int g = 0; g < 4; ++g) asm volatile("" : "+v"(lv[g]), "+v"(dvv[g]));
+  TrReads<D, 2 * TT> r0;
+  r0.issue(tra_do);
   bf16x8 pb[2], dsb[2];
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -385,8 +467,16 @@ __device__ __forceinline__ void block_tile(unsigned qt_base, unsigned dot_base, 
     pb[i >> 3][i & 7] = (__bf16)pr;
     dsb[i >> 3][i & 7] = (__bf16)(pr * (dp[i] - dvv[i >> 2][i & 3]));
   }
-  transposed_products_tile<D, TT>(tra_do, pb, dv);
-  transposed_products_tile<D, TT>(tra_q, dsb, dk);
+  TrReads<D, 2 * TT + 1> r1;
+  r1.issue(tra_do);
+  r0.template mfmas<kTrPerStep>(pb[0], dv);
+  TrReads<D, 2 * TT> r2;
+  r2.issue(tra_q);
+  r1.template mfmas<kTrPerStep>(pb[1], dv);
+  TrReads<D, 2 * TT + 1> r3;
+  r3.issue(tra_q);
+  r2.template mfmas<kTrPerStep>(dsb[0], dk);
+  r3.template mfmas<0>(dsb[1], dk);
 }
 
 template <int D, bool CAUSAL>

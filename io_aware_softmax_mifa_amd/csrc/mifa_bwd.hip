@@ -425,16 +425,75 @@ __device__ __forceinline__ f32x4 lds_read_f32x4_at256(unsigned addr) {
   return r;
 }
 
-// One 32-query tile TT of a query block: S = Q K^T and dP = dO V^T for the wave's 32 keys, then
-// P and dS, then dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries.
+// dV/dK products of one 32-query tile are deferred into the next step, where they run during
+// that step's softmax arithmetic (one wave per SIMD: no other wave overlaps them).  Only the
+// tile's P and dS (bf16) cross steps in registers; the transposed dO and Q operands are read
+// again from LDS in the next step, which is why the query blocks are triple-buffered: the
+// buffer of block j is refilled only after block j+1's first step has read it.
+struct Pending {
+  bf16x8 pb[2], dsb[2];
+};
+
+// The deferred products of tile TT, whose dO^T and Q^T operands sit in the tile pair at
+// do_base / q_base: dV^T += dO^T P, dK^T += Q^T dS, interleaved with this step's scores.
+// The transposed reads go out first (after the current tile's row reads have all landed);
+// MFMA m of the 4 kDT waits for its own pair.
+template <int D, int TT>
+struct DeferredReads {
+  static constexpr int kDT = D / 32, kReads = 8 * kDT;
+  TrReads<D, 2 * TT> do0, q0;
+  TrReads<D, 2 * TT + 1> do1, q1;
+  __device__ __forceinline__ void issue(const unsigned (&tra_do)[kDT][2], const unsigned (&tra_q)[kDT][2]) {
+    do0.issue(tra_do);
+    do1.issue(tra_do);
+    q0.issue(tra_q);
+    q1.issue(tra_q);
+  }
+  template <int M>
+  __device__ __forceinline__ void mfma_m(const Pending& pd, f32x16 (&dv)[kDT], f32x16 (&dk)[kDT]) {
+    constexpr int t = M % kDT, part = M / kDT;
+    // reads issued after this MFMA's pair: the rest of its group and the later groups
+    constexpr int after = kReads - (part * 2 * kDT + 2 * t + 2);
+    auto op = [](const i16x4& lo, const i16x4& hi) {
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    if constexpr (part == 0) {
+      lgkm_wait<kClampLgkm<after>>(do0.lo[t], do0.hi[t]);
+      dv[t] = mfma(op(do0.lo[t], do0.hi[t]), pd.pb[0], dv[t]);
+    } else if constexpr (part == 1) {
+      lgkm_wait<kClampLgkm<after>>(do1.lo[t], do1.hi[t]);
+      dv[t] = mfma(op(do1.lo[t], do1.hi[t]), pd.pb[1], dv[t]);
+    } else if constexpr (part == 2) {
+      lgkm_wait<kClampLgkm<after>>(q0.lo[t], q0.hi[t]);
+      dk[t] = mfma(op(q0.lo[t], q0.hi[t]), pd.dsb[0], dk[t]);
+    } else {
+      lgkm_wait<kClampLgkm<after>>(q1.lo[t], q1.hi[t]);
+      dk[t] = mfma(op(q1.lo[t], q1.hi[t]), pd.dsb[1], dk[t]);
+    }
+  }
+};
+
+// P and dS of score i of this lane (query row 32 TT + 8 (i/4) + 4 hf + i%4 of the block).
+template <int I>
+__device__ __forceinline__ void score(const f32x16& s, const f32x16& dp, const f32x4 (&lv)[4], const f32x4 (&dvv)[4],
+                                      float c_log2, Pending& cur) {
+  const float sv = s[I];
+  const float l2 = lv[I >> 2][I & 3] * 1.4426950408889634f;
+  const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c_log2, -l2));
+  cur.pb[I >> 3][I & 7] = (__bf16)pr;
+  cur.dsb[I >> 3][I & 7] = (__bf16)(pr * (dp[I] - dvv[I >> 2][I & 3]));
+}
+
+// One 32-query tile TT of a query block: S = Q K^T and dP = dO V^T for the wave's 32 keys; then
+// the previous tile's dV/dK products (operands at ptra_do / ptra_q, its P and dS in prev)
+// interleaved with this tile's P and dS (into cur).
 template <int D, bool CAUSAL, int TT>
-__device__ __forceinline__ void block_tile(unsigned qt_base, unsigned dot_base, unsigned rv, int ln, int hf,
-                                           const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16], bool masked, int q0,
-                                           int Nq, int my_key, int kshift, float c_log2,
-                                           const unsigned (&tra_do)[D / 32][2], const unsigned (&tra_q)[D / 32][2],
-                                           f32x16 (&dv)[D / 32], f32x16 (&dk)[D / 32]) {
-  constexpr int kDS = D / 16, kTrPerStep = 2 * (D / 32);
-  // this lane's 16 query rows of the tile: 32 TT + 8 g + 4 hf + (0..3), g = 0..3
+__device__ __forceinline__ void step(bool masked, unsigned qt_base, unsigned dot_base, unsigned rv, int ln, int hf,
+                                     const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16], int q0, int Nq,
+                                     int my_key, int kshift, float c_log2, const unsigned (&ptra_do)[D / 32][2],
+                                     const unsigned (&ptra_q)[D / 32][2], const Pending& prev, Pending& cur,
+                                     f32x16 (&dv)[D / 32], f32x16 (&dk)[D / 32]) {
+  constexpr int kDS = D / 16, kNM = 4 * (D / 32);
   f32x4 lv[4], dvv[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -442,45 +501,39 @@ __device__ __forceinline__ void block_tile(unsigned qt_base, unsigned dot_base, 
     lv[g] = lds_read_f32x4_at(ra);
     dvv[g] = lds_read_f32x4_at256(ra);
   }
-  bf16x8 qa[kDS], oa[kDS];
-  issue_rows<D>(qt_base, 32 * TT + ln, hf, qa);
-  issue_rows<D>(dot_base, 32 * TT + ln, hf, oa);
   f32x16 s, dp;
-  rows_product<D, kDS>(qa, kf, s);
-  rows_product<D, 0>(oa, vf, dp);
+  {
+    bf16x8 qa[kDS], oa[kDS];
+    issue_rows<D>(qt_base, 32 * TT + ln, hf, qa);
+    issue_rows<D>(dot_base, 32 * TT + ln, hf, oa);
+    rows_product<D, kDS>(qa, kf, s);
+    rows_product<D, 0>(oa, vf, dp);
+  }
   // every read issued so far has landed (the last wait above counted none outstanding)
 #pragma unroll
   for (int g = 0; g < 4; ++g) asm volatile("" : "+v"(lv[g]), "+v"(dvv[g]));
-  TrReads<D, 2 * TT> r0;
-  r0.issue(tra_do);
-  bf16x8 pb[2], dsb[2];
+  // Blocks on the causal diagonal or past the last query: hidden scores get -inf (P = 0).
+  if (masked) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float sv = s[i];
-    if (masked) {
+    for (int i = 0; i < 16; ++i) {
       const int qg = q0 + 32 * TT + 8 * (i >> 2) + 4 * hf + (i & 3);
       const bool vis = qg < Nq && (!CAUSAL || my_key <= qg + kshift);
-      sv = vis ? sv : -__builtin_inff();
+      s[i] = vis ? s[i] : -__builtin_inff();
     }
-    const float l2 = lv[i >> 2][i & 3] * 1.4426950408889634f;
-    const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c_log2, -l2));
-    pb[i >> 3][i & 7] = (__bf16)pr;
-    dsb[i >> 3][i & 7] = (__bf16)(pr * (dp[i] - dvv[i >> 2][i & 3]));
   }
-  TrReads<D, 2 * TT + 1> r1;
-  r1.issue(tra_do);
-  r0.template mfmas<kTrPerStep>(pb[0], dv);
-  TrReads<D, 2 * TT> r2;
-  r2.issue(tra_q);
-  r1.template mfmas<kTrPerStep>(pb[1], dv);
-  TrReads<D, 2 * TT + 1> r3;
-  r3.issue(tra_q);
-  r2.template mfmas<kTrPerStep>(dsb[0], dk);
-  r3.template mfmas<0>(dsb[1], dk);
+  DeferredReads<D, 1 - TT> pr;
+  pr.issue(ptra_do, ptra_q);
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    ((([&] {
+        if constexpr ((I * kNM) % 16 == 0) pr.template mfma_m<I * kNM / 16>(prev, dv, dk);
+      }()),
+      score<I>(s, dp, lv, dvv, c_log2, cur)),
+     ...);
+  }(std::make_integer_sequence<int, 16>{});
 }
 
 template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(D == 128 ? 1 : 2, D == 128 ? 1 : 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(1, 1)))
 void dkdv_kernel(BwdParams p) {
   using G = Geo<D>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -514,9 +567,9 @@ void dkdv_kernel(BwdParams p) {
   const float* lh = p.lse + (int64_t)bh * Nq;
   const float* dh = p.dd + (int64_t)bh * Nq;
   const unsigned base = (unsigned)(uintptr_t)(lds_void*)smem;
-  // LDS: buffer b holds Q at smem + 2b kTile, dO at smem + (2b + 1) kTile; the rows' LSE and D
-  // follow the four tiles (64 floats each, two buffers).
-  char* rowvals = smem + 4 * G::kTile;
+  // LDS: buffer u (0..2) holds Q at smem + 2u kTile, dO at smem + (2u + 1) kTile; the rows'
+  // LSE and D follow the six tiles (64 floats each, 512 bytes per buffer).
+  char* rowvals = smem + 6 * G::kTile;
   auto load_block = [&](int jq, int buf) {
     const int limit = Nq - 1 - jq * kBlk;
     dma_tile<D>(qh + (int64_t)jq * kBlk * p.sq.n, smem + 2 * buf * G::kTile, wave, lane, limit, qsb);
@@ -529,25 +582,51 @@ void dkdv_kernel(BwdParams p) {
                                        (lds_void*)(rowvals + buf * 512 + 256), 4, 0, 0);
     }
   };
+  // The first step's deferred products read buffer 2 with P = dS = 0; zero it so that those
+  // products add exactly nothing (uninitialised LDS could hold NaN patterns).
+  {
+    u32x4* z = (u32x4*)(smem + 4 * G::kTile);
+#pragma unroll
+    for (int i = 0; i < 2 * G::kTile / 16 / kThreads; ++i) z[tid + i * kThreads] = (u32x4){};
+  }
+  Pending pend0, pend1;  // tile 0 / tile 1 of the latest block
+#pragma unroll
+  for (int i = 0; i < 2; ++i) pend1.pb[i] = pend1.dsb[i] = (bf16x8){};
+  int pbuf = 2;          // buffer of the tile pending in pend1
   if (jb < n_qb) load_block(jb, 0);
   for (int jq = jb; jq < n_qb; ++jq) {
     wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    const int bf = (jq - jb) & 1;
-    if (jq + 1 < n_qb) load_block(jq + 1, bf ^ 1);
-    const unsigned qt_base = base + 2 * bf * G::kTile, dot_base = qt_base + G::kTile;
-    // this lane's 16 query rows of tile tt: 32 tt + 8 g + 4 hf + (0..3), g = 0..3
-    const unsigned rv = base + 4 * G::kTile + bf * 512;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // block jq has landed; buffer (jq+1) mod 3 was last read two steps ago
+    const int u = (jq - jb) % 3;
+    if (jq + 1 < n_qb) load_block(jq + 1, u == 2 ? 0 : u + 1);
+    const unsigned qt_base = base + 2 * u * G::kTile, dot_base = qt_base + G::kTile;
+    const unsigned pq_base = base + 2 * pbuf * G::kTile, pdo_base = pq_base + G::kTile;
+    const unsigned rv = base + 6 * G::kTile + u * 512;
     const int q0 = jq * kBlk;
     const bool masked = (CAUSAL && q0 + kshift < tile_key0 + kRows - 1) || q0 + kBlk > Nq;
-    unsigned tra_do[G::kDT][2], tra_q[G::kDT][2];
+    unsigned tra_do[G::kDT][2], tra_q[G::kDT][2], ptra_do[G::kDT][2], ptra_q[G::kDT][2];
     tr_addrs<D>(dot_base, lane, tra_do);
     tr_addrs<D>(qt_base, lane, tra_q);
-    [&]<int... TT>(std::integer_sequence<int, TT...>) {
-      ((block_tile<D, CAUSAL, TT>(qt_base, dot_base, rv, ln, hf, kf, vf, masked, q0, Nq, my_key, kshift, p.c_log2,
-                                  tra_do, tra_q, dv, dk)),
-       ...);
-    }(std::make_integer_sequence<int, 2>{});
+    tr_addrs<D>(pdo_base, lane, ptra_do);
+    tr_addrs<D>(pq_base, lane, ptra_q);
+    const float c = p.c_log2;
+    step<D, CAUSAL, 0>(masked, qt_base, dot_base, rv, ln, hf, kf, vf, q0, Nq, my_key, kshift, c, ptra_do, ptra_q,
+                       pend1, pend0, dv, dk);
+    step<D, CAUSAL, 1>(masked, qt_base, dot_base, rv, ln, hf, kf, vf, q0, Nq, my_key, kshift, c, tra_do, tra_q,
+                       pend0, pend1, dv, dk);
+    pbuf = u;
+  }
+  // the last tile's dV/dK products
+  {
+    const unsigned pq_base = base + 2 * pbuf * G::kTile, pdo_base = pq_base + G::kTile;
+    unsigned ptra_do[G::kDT][2], ptra_q[G::kDT][2];
+    tr_addrs<D>(pdo_base, lane, ptra_do);
+    tr_addrs<D>(pq_base, lane, ptra_q);
+    DeferredReads<D, 1> pr;
+    pr.issue(ptra_do, ptra_q);
+    [&]<int... M>(std::integer_sequence<int, M...>) { (pr.template mfma_m<M>(pend1, dv, dk), ...); }(
+        std::make_integer_sequence<int, 4 * G::kDT>{});
   }
   wait_vmcnt<0>();
   if (my_key < Nk) {
@@ -556,7 +635,10 @@ void dkdv_kernel(BwdParams p) {
   }
 }
 
-constexpr int kRowValsBytes = 2 * 512;
+constexpr int kRowValsBytes = 3 * 512;
+// dkdv: three Q/dO buffer pairs and their row values
+template <int D>
+constexpr int kDkdvLds = 6 * Geo<D>::kTile + kRowValsBytes;
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdParams& p, const void* o, Strides so, int o_bf16, float* dd, hipStream_t s) {
@@ -570,7 +652,7 @@ hipError_t launch_bwd(const BwdParams& p, const void* o, Strides so, int o_bf16,
   static const hipError_t a1 =
       hipFuncSetAttribute((const void*)dq_kernel<D, CAUSAL>, hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
   static const hipError_t a2 = hipFuncSetAttribute((const void*)dkdv_kernel<D, CAUSAL>,
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds + kRowValsBytes);
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, kDkdvLds<D>);
   if (a1 != hipSuccess) return a1;
   if (a2 != hipSuccess) return a2;
   const unsigned gq = (unsigned)((int64_t)p.BH * ((p.Nq + kRows - 1) / kRows));
@@ -578,7 +660,7 @@ hipError_t launch_bwd(const BwdParams& p, const void* o, Strides so, int o_bf16,
   hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(gq), dim3(kThreads), G::kLds, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(gk), dim3(kThreads), G::kLds + kRowValsBytes, s, p);
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(gk), dim3(kThreads), kDkdvLds<D>, s, p);
   return hipGetLastError();
 }
 

@@ -236,3 +236,19 @@ def make_grad_output(B: int, H: int, Nq: int, d: int, seed: int) -> torch.Tensor
     """bf16 CPU tensor dO [B, H, Nq, d] ~ N(0, 1): the upstream gradient of a backward pass."""
     g = torch.Generator().manual_seed(seed + 7919)
     return torch.randn((B, H, Nq, d), generator=g).to(torch.bfloat16)
+
+
+def sample_rows_in_heads(B: int, H: int, N: int, heads: int, per_head: int, seed: int) -> torch.Tensor:
+    """Seeded (b, h, i) rows confined to `heads` distinct (b, h) pairs, `per_head` rows each,
+    always including i in {0, 1, 127, 128, N-1} (those that exist).  For checks whose cost
+    grows with the number of distinct heads (key-side gradients need a whole head)."""
+    g = torch.Generator().manual_seed(seed + 2000)
+    pairs = torch.randperm(B * H, generator=g)[:heads].tolist()
+    out = []
+    for ph in pairs:
+        b, h = divmod(ph, H)
+        edges = [i for i in (0, 1, 127, 128, N - 1) if i < N]
+        rest = [i for i in torch.randperm(N, generator=g).tolist() if i not in edges]
+        chosen = sorted(set(edges + rest[: max(0, per_head - len(edges))]))
+        out.extend((b, h, i) for i in chosen)
+    return torch.tensor(out, dtype=torch.int64)

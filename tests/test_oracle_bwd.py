@@ -107,8 +107,42 @@ def pin_query_rescaling():
     np.testing.assert_allclose(dv2, dv, atol=1e-13)
 
 
+def pin_rows_against_torch():
+    for causal, nq, nk in ((True, 9, 9), (False, 6, 10), (True, 5, 12)):
+        q, k, v = _rand(23, 1, 2, nq, 8), _rand(24, 1, 2, nk, 8), _rand(25, 1, 2, nk, 8)
+        do = _rand(26, 1, 2, nq, 8)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        mask = torch.ones(nq, nk, dtype=torch.bool).tril(diagonal=nk - nq) if causal else None
+        torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.3).backward(
+            torch.tensor(do))
+        q_rows = [(0, h, i) for h in range(2) for i in range(nq)]
+        k_rows = [(0, h, j) for h in range(2) for j in range(nk)]
+        dq, dk, dv = OB.attention_bwd_fp64_rows(q, k, v, do, q_rows, k_rows, causal=causal, scale=0.3)
+        np.testing.assert_allclose(dq, tq.grad.numpy()[0].reshape(-1, 8), atol=1e-10)
+        np.testing.assert_allclose(dk, tk.grad.numpy()[0].reshape(-1, 8), atol=1e-10)
+        np.testing.assert_allclose(dv, tv.grad.numpy()[0].reshape(-1, 8), atol=1e-10)
+
+
+def pin_rows_match_full_in_chunks():
+    saved = OB._CHUNK
+    try:
+        OB._CHUNK = 3   # several query chunks, the last one partial
+        for causal, nq, nk in ((True, 11, 11), (True, 7, 13), (False, 10, 4)):
+            q, k, v = _rand(27, 2, 2, nq, 4), _rand(28, 2, 2, nk, 4), _rand(29, 2, 2, nk, 4)
+            do = _rand(30, 2, 2, nq, 4)
+            fq, fk, fv, _ = OB.attention_bwd_fp64(q, k, v, do, causal=causal, scale=0.8)
+            q_rows = [(1, 0, nq - 1), (0, 1, 0), (1, 1, nq // 2)]
+            k_rows = [(0, 0, 0), (1, 1, nk - 1), (1, 0, nk // 2), (0, 1, 1)]
+            dq, dk, dv = OB.attention_bwd_fp64_rows(q, k, v, do, q_rows, k_rows, causal=causal, scale=0.8)
+            np.testing.assert_allclose(dq, [fq[b, h, i] for b, h, i in q_rows], atol=1e-12)
+            np.testing.assert_allclose(dk, [fk[b, h, j] for b, h, j in k_rows], atol=1e-12)
+            np.testing.assert_allclose(dv, [fv[b, h, j] for b, h, j in k_rows], atol=1e-12)
+    finally:
+        OB._CHUNK = saved
+
+
 PINS = [pin_finite_differences, pin_torch_autograd, pin_single_key, pin_key_gradients_sum_to_zero,
-        pin_query_rescaling]
+        pin_query_rescaling, pin_rows_against_torch, pin_rows_match_full_in_chunks]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)

@@ -47,3 +47,17 @@ def test_configs_table():
     c4 = W.by_name("C4")
     assert c4.shape == (1, 32, 16384, 128) and c4.causal and c4.oracle_rows == 256
     assert W.by_name("C5").dist == "stress"
+
+
+def test_sample_rows_in_heads():
+    from io_aware_softmax_mifa_amd import workloads as W
+
+    r = W.sample_rows_in_heads(1, 32, 16384, 2, 32, 104)
+    assert r.shape == (64, 3)
+    assert len({(int(b), int(h)) for b, h, _ in r}) == 2
+    for b, h in {(int(b), int(h)) for b, h, _ in r}:
+        rows = {int(i) for bb, hh, i in r if (int(bb), int(hh)) == (b, h)}
+        assert {0, 1, 127, 128, 16383} <= rows and len(rows) == 32
+    assert torch.equal(r, W.sample_rows_in_heads(1, 32, 16384, 2, 32, 104))
+    small = W.sample_rows_in_heads(2, 2, 3, 3, 2, 1)      # N below the edge rows
+    assert all(0 <= int(i) < 3 for _, _, i in small)

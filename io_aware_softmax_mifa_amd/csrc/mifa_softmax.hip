@@ -111,40 +111,96 @@ __device__ __forceinline__ float wave_sum(float s) {
 // ---- register-resident rows ----------------------------------------------------------------
 // WPR waves per row (1 or 4), EPT elements per thread.  Thread t of a row group of G = 64 WPR
 // threads holds vector k (k = 0 .. EPT/V - 1) at element offset (k G + t) V.
-template <typename T, int WPR, int EPT>
-__global__ __launch_bounds__(kThreads) void softmax_resident(const T* __restrict__ x, T* __restrict__ y,
-                                                              float* __restrict__ lse, int64_t rows, int cols,
-                                                              float c, int vec_ok) {
+// bf16 rows of 64 or more elements per thread keep the raw bf16 pairs in registers (EPT/2
+// per thread instead of EPT floats) and widen them again in each pass; the passes then
+// recompute exp2(c x - m) where the float version kept it.  The arithmetic is the same
+// sequence of float operations, so the results are identical, and twice as many waves fit
+// on a SIMD to overlap one row's loads with another's stores (measured on MI355X: 32,768-element
+// rows 18% faster; at 32 elements per thread occupancy was already high and the recomputed
+// exponentials made 2,048-element rows 9% slower).
+template <typename T, int EPT>
+constexpr bool kPackedRow = sizeof(T) == 2 && EPT >= 64;
+
+// NT threads per workgroup (NT/64 waves), WPR waves per row, EPT elements per thread.
+template <typename T, int WPR, int EPT, int NT>
+__global__ __launch_bounds__(NT) void softmax_resident(const T* __restrict__ x, T* __restrict__ y,
+                                                       float* __restrict__ lse, int64_t rows, int cols, float c,
+                                                       int vec_ok) {
   using E = Elem<T>;
-  constexpr int V = E::kVec, G = 64 * WPR, NV = EPT / V;
+  constexpr int V = E::kVec, G = 64 * WPR, NV = EPT / V, NW = NT / 64;
+  constexpr bool kPacked = kPackedRow<T, EPT>;
   static_assert(EPT % V == 0, "whole vectors per thread");
-  __shared__ float red[2][4];
+  static_assert(NW % WPR == 0, "whole rows per workgroup");
+  __shared__ float red[2][NW];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int w0 = wave - wave % WPR;  // first wave of this row
   const int t = tid & (G - 1);
-  const int64_t row = (int64_t)blockIdx.x * (4 / WPR) + wave / WPR;
+  const int64_t row = (int64_t)blockIdx.x * (NW / WPR) + wave / WPR;
   const bool live = row < rows;
   const T* xr = x + (live ? row : 0) * (int64_t)cols;
   T* yr = y + (live ? row : 0) * (int64_t)cols;
 
   // Element (k, i) of this thread: (k G + t) V + i with 16-byte vectors, or (k V + i) G + t with
-  // element loads (consecutive lanes then read consecutive elements).
-  float v[EPT];
+  // element loads (consecutive lanes then read consecutive elements).  It is v[k V + i], or
+  // the low (i even) / high half of raw[(k V + i) / 2] when packed.
+  float v[kPacked ? 1 : EPT];
+  unsigned raw[kPacked ? EPT / 2 : 1];
+  constexpr unsigned kNegInfBits = 0xff80u;  // bf16 -inf
+  // The compiler would otherwise keep the widened values of one pass for the next (they are
+  // the same expressions), undoing the packing: each pass starts from registers it cannot see
+  // through.
+  auto opaque = [&]() {
+    if constexpr (kPacked) {
+#pragma unroll
+      for (int j = 0; j < EPT / 2; ++j) asm volatile("" : "+v"(raw[j]));
+    }
+  };
+  auto elem = [&](int idx) -> float {
+    if constexpr (kPacked) {
+      const unsigned w = raw[idx >> 1];
+      return __builtin_bit_cast(float, (idx & 1) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+      return v[idx];
+    }
+  };
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     if (vec_ok) {
       const int e0 = (k * G + t) * V;
       if (live && e0 + V <= cols) {
-        E::load_vec(xr + e0, v + k * V);
+        if constexpr (kPacked) {
+          const u32x4 r = *(const u32x4*)(xr + e0);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) raw[k * 4 + j] = r[j];
+        } else {
+          E::load_vec(xr + e0, v + k * V);
+        }
       } else {
 #pragma unroll
-        for (int i = 0; i < V; ++i) v[k * V + i] = (live && e0 + i < cols) ? E::load(xr + e0 + i) : -__builtin_inff();
+        for (int i = 0; i < V; ++i) {
+          const bool in = live && e0 + i < cols;
+          if constexpr (kPacked) {
+            const unsigned b = in ? (unsigned)__builtin_bit_cast(unsigned short, xr[e0 + i]) : kNegInfBits;
+            if (i & 1) raw[(k * V + i) >> 1] |= b << 16;
+            else raw[(k * V + i) >> 1] = b;
+          } else {
+            v[k * V + i] = in ? E::load(xr + e0 + i) : -__builtin_inff();
+          }
+        }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         const int e = (k * V + i) * G + t;
-        v[k * V + i] = (live && e < cols) ? E::load(xr + e) : -__builtin_inff();
+        const bool in = live && e < cols;
+        if constexpr (kPacked) {
+          const unsigned b = in ? (unsigned)__builtin_bit_cast(unsigned short, xr[e]) : kNegInfBits;
+          if (i & 1) raw[(k * V + i) >> 1] |= b << 16;
+          else raw[(k * V + i) >> 1] = b;
+        } else {
+          v[k * V + i] = in ? E::load(xr + e) : -__builtin_inff();
+        }
       }
     }
   }
@@ -153,47 +209,66 @@ __global__ __launch_bounds__(kThreads) void softmax_resident(const T* __restrict
   float m = -__builtin_inff();
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    v[i] = scaled(v[i], c);
-    m = fmax2(m, v[i]);
+    const float sv = scaled(elem(i), c);
+    if constexpr (!kPacked) v[i] = sv;
+    m = fmax2(m, sv);
   }
   m = wave_max(m);
   if constexpr (WPR > 1) {
     if ((tid & 63) == 0) red[0][wave] = m;
     __syncthreads();
-    m = fmax2(fmax2(red[0][0], red[0][1]), fmax2(red[0][2], red[0][3]));
+    m = red[0][w0];
+#pragma unroll
+    for (int w = 1; w < WPR; ++w) m = fmax2(m, red[0][w0 + w]);
   }
   float l = 0.f;
+  opaque();
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    v[i] = __builtin_amdgcn_exp2f(v[i] - m);
-    l += v[i];
+    if constexpr (kPacked) {
+      l += __builtin_amdgcn_exp2f(scaled(elem(i), c) - m);
+    } else {
+      v[i] = __builtin_amdgcn_exp2f(v[i] - m);
+      l += v[i];
+    }
   }
   l = wave_sum(l);
   if constexpr (WPR > 1) {
     if ((tid & 63) == 0) red[1][wave] = l;
     __syncthreads();
-    l = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    if constexpr (WPR == 4) {
+      l = (red[1][w0] + red[1][w0 + 1]) + (red[1][w0 + 2] + red[1][w0 + 3]);
+    } else {
+      l = red[1][w0];
+#pragma unroll
+      for (int w = 1; w < WPR; ++w) l += red[1][w0 + w];
+    }
   }
   if (!live) return;
   const float inv = 1.f / l;
+  opaque();
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
+    float o[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) v[k * V + i] *= inv;
+    for (int i = 0; i < V; ++i) {
+      if constexpr (kPacked) o[i] = __builtin_amdgcn_exp2f(scaled(elem(k * V + i), c) - m) * inv;
+      else o[i] = v[k * V + i] * inv;
+    }
     if (vec_ok) {
       const int e0 = (k * G + t) * V;
       if (e0 + V <= cols) {
-        E::store_vec(yr + e0, v + k * V);
+        E::store_vec(yr + e0, o);
       } else {
 #pragma unroll
         for (int i = 0; i < V; ++i)
-          if (e0 + i < cols) E::store(yr + e0 + i, v[k * V + i]);
+          if (e0 + i < cols) E::store(yr + e0 + i, o[i]);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         const int e = (k * V + i) * G + t;
-        if (e < cols) E::store(yr + e, v[k * V + i]);
+        if (e < cols) E::store(yr + e, o[i]);
       }
     }
   }
@@ -299,19 +374,21 @@ __global__ __launch_bounds__(kThreads) void softmax_stream(const T* __restrict__
   if (lse && tid == 0) lse[row] = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
 }
 
-template <typename T, int WPR, int EPT>
+template <typename T, int WPR, int EPT, int NT = kThreads>
 hipError_t launch_resident(const void* x, void* y, float* lse, int64_t rows, int cols, float c, int vec_ok,
                            hipStream_t s) {
-  const int64_t blocks = (rows + (4 / WPR) - 1) / (4 / WPR);
-  hipLaunchKernelGGL((softmax_resident<T, WPR, EPT>), dim3((unsigned)blocks), dim3(kThreads), 0, s, (const T*)x,
-                     (T*)y, lse, rows, cols, c, vec_ok);
+  constexpr int rpb = NT / 64 / WPR;
+  const int64_t blocks = (rows + rpb - 1) / rpb;
+  hipLaunchKernelGGL((softmax_resident<T, WPR, EPT, NT>), dim3((unsigned)blocks), dim3(NT), 0, s, (const T*)x, (T*)y,
+                     lse, rows, cols, c, vec_ok);
   return hipGetLastError();
 }
 
-// Launch choice by row length: one wave per row up to 64*64 elements, one workgroup with the row
-// in registers up to 256*128 (128 values per thread: two waves per SIMD still fit), streaming
-// (two reads) beyond.  Measured on MI355X: keeping 32,768-element rows in registers runs
-// 1.2-1.5x faster than staging them in LDS or streaming them.  EPT is the smallest whole number of vectors that covers the row.
+// Launch choice by row length: one wave per row up to 64*64 elements, one 256-thread workgroup
+// with the row in registers up to 256*128, one 1024-thread workgroup with the row in registers
+// up to 1024*128 (bf16) or 1024*64 (float), streaming (two reads) beyond.  Measured on MI355X:
+// keeping 32,768-element rows in registers runs 1.2-1.5x faster than staging them in LDS or
+// streaming them.  EPT is the smallest whole number of vectors that covers the row.
 template <typename T>
 hipError_t dispatch_softmax(const void* x, void* y, float* lse, int64_t rows, int cols, float c, int vec_ok,
                             hipStream_t s) {
@@ -327,6 +404,13 @@ hipError_t dispatch_softmax(const void* x, void* y, float* lse, int64_t rows, in
   if (cols <= 256 * 32) return launch_resident<T, 4, 32>(x, y, lse, rows, cols, c, vec_ok, s);
   if (cols <= 256 * 64) return launch_resident<T, 4, 64>(x, y, lse, rows, cols, c, vec_ok, s);
   if (cols <= 256 * 128) return launch_resident<T, 4, 128>(x, y, lse, rows, cols, c, vec_ok, s);
+  // Up to 131,072 bf16 (65,536 float) elements: one 1024-thread workgroup per row, the row still
+  // in registers (bf16 packed two per register), so it is read once instead of twice.
+  if constexpr (sizeof(T) == 2) {
+    if (cols <= 1024 * 128) return launch_resident<T, 16, 128, 1024>(x, y, lse, rows, cols, c, vec_ok, s);
+  } else {
+    if (cols <= 1024 * 64) return launch_resident<T, 16, 64, 1024>(x, y, lse, rows, cols, c, vec_ok, s);
+  }
   hipLaunchKernelGGL(softmax_stream<T>, dim3((unsigned)rows), dim3(kThreads), 0, s, (const T*)x, (T*)y, lse, cols, c,
                      vec_ok);
   return hipGetLastError();

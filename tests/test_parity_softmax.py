@@ -61,7 +61,7 @@ def full_case(rows, cols, dtype, std, seed, scale=1.0):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("cols", [1, 2, 7, 8, 63, 64, 65, 255, 256, 511, 512, 513, 1000, 2047, 2048, 4095, 4096,
                                   4097, 8191, 8192, 16383, 16384, 16385, 20000, 32767, 32768, 32769, 40000,
-                                  100003])
+                                  65536, 65537, 100003, 131072, 131073])
 def test_lengths(cols, dtype):
     full_case(5, cols, dtype, 2.0, seed=cols)
 

@@ -89,6 +89,30 @@ def blas_threads() -> int:
     return 1
 
 
+def host_info() -> dict:
+    """What the oracle ran on: logical CPUs, the ones this process may use, the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"host_cpus": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
+def event_stats(starts, ends) -> dict:
+    """Median and minimum per-call milliseconds from paired HIP events."""
+    ms = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+    return {"call_ms_median": ms[len(ms) // 2], "call_ms_min": ms[0]}
+
+
 def cpu_baseline(w, q, k, v, scale, rows_count: int):
     """The float64 oracle as it stands, timed on this host on a bounded sample of rows."""
     from io_aware_softmax_mifa_amd import workloads as W
@@ -101,7 +125,7 @@ def cpu_baseline(w, q, k, v, scale, rows_count: int):
     # Credit each sampled row with the per-row share of the step's FLOP convention.
     per_row = flops(w) / (w.B * w.H * w.N)
     value = rows.shape[0] * per_row / dt / 1e12
-    return {
+    out = {
         "value": value,
         "unit": "TFLOP/s",
         "cores": blas_threads(),
@@ -109,8 +133,12 @@ def cpu_baseline(w, q, k, v, scale, rows_count: int):
         "sample": (f"{rows.shape[0]} seeded query rows of the same workload (float64 NumPy oracle, full "
                    f"score row per query), {dt:.2f} s; credited {per_row:.3e} FLOP per row"),
         "seconds": dt,
-        "host_cpus": os.cpu_count(),
+        # every row costs the oracle the same (it scores the full row, then masks), so the whole
+        # workload would take about this long: an extrapolation, not a run
+        "extrapolated_full_oracle_seconds": dt * (w.B * w.H * w.N) / rows.shape[0],
     }
+    out.update(host_info())
+    return out
 
 
 def copy_calibration(dev):
@@ -155,7 +183,7 @@ def softmax_cpu_baseline(w, x, rows_count: int):
         "sample": (f"{rows.shape[0]} of the workload's {w.rows} rows (float64 NumPy oracle), {dt:.2f} s; "
                    f"credited {per_row:.0f} compulsory bytes per row"),
         "seconds": dt,
-        "host_cpus": os.cpu_count(),
+        **host_info(),
     }
 
 
@@ -265,8 +293,9 @@ def bench_decode(args):
             "kind": "oracle",
             "sample": f"every one of the {rows.shape[0]} query rows (float64 NumPy oracle), {dt:.2f} s",
             "seconds": dt,
-            "host_cpus": os.cpu_count(),
+            **host_info(),
         }
+    out["config"].update(event_stats(starts, ends))
     print(json.dumps(out), flush=True)
 
 
@@ -340,6 +369,7 @@ def bench_softmax(args):
         },
     }
     out["cpu_baseline"] = None if args.no_cpu_baseline else softmax_cpu_baseline(w, x, args.cpu_rows_softmax)
+    out["config"].update(event_stats(starts, ends))
     print(json.dumps(out), flush=True)
 
 
@@ -459,8 +489,9 @@ def bench_backward(args):
                        f"smaller problem), float64 NumPy oracle with the full P materialised, {dt:.2f} s; "
                        f"credited with the same 10 d FLOPs per visible pair"),
             "seconds": dt,
-            "host_cpus": os.cpu_count(),
+            **host_info(),
         }
+    out["config"].update(event_stats(starts, ends))
     print(json.dumps(out), flush=True)
 
 
@@ -572,6 +603,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, scale, args.cpu_rows)
     else:
         out["cpu_baseline"] = None
+    out["config"].update(event_stats(starts, ends))
     print(json.dumps(out), flush=True)
 
 

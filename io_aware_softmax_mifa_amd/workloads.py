@@ -17,7 +17,7 @@ import math
 
 import torch
 
-__all__ = ["Workload", "CONFIGS", "by_name", "fp32_scale", "make_inputs", "sample_rows", "DecodeWorkload",
+__all__ = ["Workload", "CONFIGS", "SHARD_CONFIGS", "by_name", "fp32_scale", "make_inputs", "sample_rows", "DecodeWorkload",
            "DECODE_CONFIGS", "decode_by_name", "make_rect_inputs", "SoftmaxWorkload",
            "SOFTMAX_CONFIGS", "softmax_by_name", "make_softmax_input", "sample_softmax_rows"]
 
@@ -55,8 +55,15 @@ CONFIGS = [
 ]
 
 
+# One GPU's share of C4 when its 32 heads are split over 8 GPUs with no communication (4 heads
+# per GPU): what a single GPU shows of the head-sharded path.
+SHARD_CONFIGS = [
+    Workload("C4-shard", 1, 4, 16384, 128, True, 104, oracle_rows=128),
+]
+
+
 def by_name(name: str) -> Workload:
-    for w in CONFIGS:
+    for w in CONFIGS + SHARD_CONFIGS:
         if w.name == name:
             return w
     raise KeyError(name)

@@ -66,7 +66,7 @@ def test_small_configs_full(name):
     full_case(w.B, w.H, w.N, w.d, w.causal, w.seed, w.dist)
 
 
-@pytest.mark.parametrize("name", ["C3", "C4", "C5"])
+@pytest.mark.parametrize("name", ["C3", "C4", "C5", "C4-shard"])
 def test_large_configs_sampled(name):
     """Full-size launch; every row of two heads plus 256 seeded sampled rows checked."""
     w = W.by_name(name)

@@ -16,9 +16,10 @@
 //    S^T = K Q^T and dP^T = V dO^T on MFMA, then dS^T, and accumulates dQ^T += K^T dS^T (K^T
 //    read from the K tile with the transposing LDS read).
 //  * dkdv: one workgroup per (b*h, 128-key tile), the roles swapped: each wave keeps 32 keys
-//    of K and V in registers, streams Q and dO blocks of 64 queries (with their LSE and D),
-//    computes S = Q K^T and dP = dO V^T, then P and dS, and accumulates dV^T += dO^T P and
-//    dK^T += Q^T dS.
+//    of K and V in registers, streams Q and dO blocks of 64 queries (with their LSE and D,
+//    three buffers), computes S = Q K^T and dP = dO V^T, then P and dS, and accumulates
+//    dV^T += dO^T P and dK^T += Q^T dS, each 32-query tile's products running during the next
+//    tile's score arithmetic.
 // In both, the probabilities / dS feed the second product straight from the accumulator
 // layout (the contraction index inside one MFMA is a free permutation), as in the forward.
 #include <hip/hip_runtime.h>
@@ -47,7 +48,7 @@ struct Geo {
   static constexpr int kRowsPerInst = 64 / kChunksPerRow;
   static constexpr int kInstPerTile = kBlk / kRowsPerInst;
   static constexpr int kInstPerWave = kInstPerTile / kWaves;
-  static constexpr int kLds = 2 * 2 * kTile;        // two tensors, double buffered
+  static constexpr int kLds = 2 * 2 * kTile;        // dq: two tensors (K, V), double buffered
   static_assert(kInstPerWave * kWaves == kInstPerTile, "tile splits evenly over the waves");
 };
 

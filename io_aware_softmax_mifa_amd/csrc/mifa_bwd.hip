@@ -39,7 +39,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;  // rows (queries or keys) a workgroup owns
 constexpr int kBlk = 64;            // rows of a streamed block (keys or queries)
 
-template <int D>
+template <int D, int W = kWaves>
 struct Geo {
   static constexpr int kDS = D / 16;                // 16-wide d slices
   static constexpr int kDT = D / 32;                // 32-row d tiles of a transposed product
@@ -47,9 +47,9 @@ struct Geo {
   static constexpr int kChunksPerRow = D / 8;       // 16-byte chunks per row
   static constexpr int kRowsPerInst = 64 / kChunksPerRow;
   static constexpr int kInstPerTile = kBlk / kRowsPerInst;
-  static constexpr int kInstPerWave = kInstPerTile / kWaves;
+  static constexpr int kInstPerWave = kInstPerTile / W;
   static constexpr int kLds = 2 * 2 * kTile;        // dq: two tensors (K, V), double buffered
-  static_assert(kInstPerWave * kWaves == kInstPerTile, "tile splits evenly over the waves");
+  static_assert(kInstPerWave * W == kInstPerTile, "tile splits evenly over the waves");
 };
 
 // ---- tiles in LDS --------------------------------------------------------------------------
@@ -67,11 +67,12 @@ __device__ __forceinline__ int swz_b(int r) {
 
 // A block of kBlk rows x D bf16, rows of D*2 bytes, 16-byte chunk c of row r at c ^ swz_b<D>(r).
 // DMA instruction t of this wave covers rows (wave*kInstPerWave + t)*kRowsPerInst ...; rows past
-// row_limit are clamped to it (the last, partial block).  Source rows are rsb bytes apart.
-template <int D>
+// row_limit are clamped to it (the last, partial block).  Source rows are rsb bytes apart; the
+// workgroup's W waves share the tile.
+template <int D, int W = kWaves>
 __device__ __forceinline__ void dma_tile(const __bf16* src, char* dst, int wave, int lane, int row_limit,
                                          unsigned rsb) {
-  using G = Geo<D>;
+  using G = Geo<D, W>;
   const char* s = (const char*)src;
 #pragma unroll
   for (int t = 0; t < G::kInstPerWave; ++t) {
@@ -278,10 +279,13 @@ __global__ __launch_bounds__(64) void row_dot_kernel(const __bf16* __restrict__ 
 }
 
 // ---- dQ ------------------------------------------------------------------------------------
-template <int D, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+// W waves of 32 query rows each: 4 (two workgroups per CU) or, for long sequences, 8 (one
+// per CU; every K/V block in LDS then serves 256 queries).
+template <int D, bool CAUSAL, int W>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * W, 64 * W), amdgpu_waves_per_eu(2, 2)))
 void dq_kernel(BwdParams p) {
-  using G = Geo<D>;
+  using G = Geo<D, W>;
+  constexpr int kQRows = 32 * W;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -290,10 +294,10 @@ void dq_kernel(BwdParams p) {
   // Workgroup w runs on XCD w % 8, so with BH a multiple of 8 all tiles of a head share one
   // XCD's L2.  Causal tiles go heaviest first: tiles that start together have about the same
   // length and stream the same K/V blocks in step, which keeps those blocks in L2.
-  const int n_qt = (Nq + kRows - 1) / kRows;
+  const int n_qt = (Nq + kQRows - 1) / kQRows;
   const int bh = blockIdx.x % BH, rank = blockIdx.x / BH;
   const int qt = CAUSAL ? n_qt - 1 - rank : rank;
-  const int my_row = qt * kRows + wave * 32 + ln;
+  const int my_row = qt * kQRows + wave * 32 + ln;
 
   const int b = bh / p.H, h = bh - b * p.H;
   bf16x8 qf[G::kDS], dof[G::kDS];
@@ -309,9 +313,9 @@ void dq_kernel(BwdParams p) {
   const int n_kb = (Nk + kBlk - 1) / kBlk;
   int nblk = n_kb, j_mask = Nk / kBlk;
   if (CAUSAL) {
-    const int last_row = min(Nq - 1, qt * kRows + kRows - 1);
+    const int last_row = min(Nq - 1, qt * kQRows + kQRows - 1);
     nblk = min(n_kb, (last_row + kshift) / kBlk + 1);
-    j_mask = min(j_mask, (qt * kRows + kshift) / kBlk);
+    j_mask = min(j_mask, (qt * kQRows + kshift) / kBlk);
   }
   const __bf16* kh = p.k + b * p.sk.b + h * p.sk.h;
   const __bf16* vh = p.v + b * p.sv.b + h * p.sv.h;
@@ -320,8 +324,8 @@ void dq_kernel(BwdParams p) {
   const int my_pos = my_row + kshift;
 
   // Buffer bf holds K at smem + 2 bf kTile and V at smem + (2 bf + 1) kTile.
-  dma_tile<D>(kh, smem, wave, lane, Nk - 1, ksb);
-  dma_tile<D>(vh, smem + G::kTile, wave, lane, Nk - 1, vsb);
+  dma_tile<D, W>(kh, smem, wave, lane, Nk - 1, ksb);
+  dma_tile<D, W>(vh, smem + G::kTile, wave, lane, Nk - 1, vsb);
   for (int j = 0; j < nblk; ++j) {
     wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();  // block j has landed for every wave; block j-1 is done
@@ -329,8 +333,8 @@ void dq_kernel(BwdParams p) {
     if (j + 1 < nblk) {
       const int nb = (j + 1) & 1;
       const int limit = Nk - 1 - (j + 1) * kBlk;
-      dma_tile<D>(kh + (int64_t)(j + 1) * kBlk * p.sk.n, smem + 2 * nb * G::kTile, wave, lane, limit, ksb);
-      dma_tile<D>(vh + (int64_t)(j + 1) * kBlk * p.sv.n, smem + (2 * nb + 1) * G::kTile, wave, lane, limit, vsb);
+      dma_tile<D, W>(kh + (int64_t)(j + 1) * kBlk * p.sk.n, smem + 2 * nb * G::kTile, wave, lane, limit, ksb);
+      dma_tile<D, W>(vh + (int64_t)(j + 1) * kBlk * p.sv.n, smem + (2 * nb + 1) * G::kTile, wave, lane, limit, vsb);
     }
     const unsigned kt_base = base + 2 * bf * G::kTile, vt_base = kt_base + G::kTile;
     f32x16 s[2], dp[2];
@@ -651,14 +655,23 @@ hipError_t launch_bwd(const BwdParams& p, const void* o, Strides so, int o_bf16,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static const hipError_t a1 =
-      hipFuncSetAttribute((const void*)dq_kernel<D, CAUSAL>, hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
+      hipFuncSetAttribute((const void*)dq_kernel<D, CAUSAL, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
+  static const hipError_t a3 =
+      hipFuncSetAttribute((const void*)dq_kernel<D, CAUSAL, 8>, hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
   static const hipError_t a2 = hipFuncSetAttribute((const void*)dkdv_kernel<D, CAUSAL>,
                                                    hipFuncAttributeMaxDynamicSharedMemorySize, kDkdvLds<D>);
   if (a1 != hipSuccess) return a1;
+  if (a3 != hipSuccess) return a3;
   if (a2 != hipSuccess) return a2;
-  const unsigned gq = (unsigned)((int64_t)p.BH * ((p.Nq + kRows - 1) / kRows));
+  // 8-wave dq workgroups for long sequences with at least one such workgroup per CU
+  const int64_t big_q = (int64_t)p.BH * ((p.Nq + 255) / 256);
+  const bool dq8 = p.Nq > 4096 && big_q >= 256;
+  const unsigned gq = (unsigned)(dq8 ? big_q : (int64_t)p.BH * ((p.Nq + kRows - 1) / kRows));
   const unsigned gk = (unsigned)((int64_t)p.BH * ((p.Nk + kRows - 1) / kRows));
-  hipLaunchKernelGGL((dq_kernel<D, CAUSAL>), dim3(gq), dim3(kThreads), G::kLds, s, p);
+  if (dq8)
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, 8>), dim3(gq), dim3(512), G::kLds, s, p);
+  else
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, 4>), dim3(gq), dim3(kThreads), G::kLds, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(gk), dim3(kThreads), kDkdvLds<D>, s, p);

@@ -160,7 +160,7 @@ int64_t mifa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t N
  *   dO       bf16 [B, H, Nq, d]: gradient of the loss with respect to o.  Read only.
  *   dq       float32 [B, H, Nq, d]; dk, dv float32 [B, H, Nk, d].  Fully overwritten.
  *   workspace  device memory of at least mifa_bwd_workspace_bytes(B, H, Nq) bytes, 16-byte
- *            aligned; overwritten (it holds D).  Not to be touched until the stream has passed
+ *            aligned; overwritten (it holds D and the LSE in log2 units).  Not to be touched until the stream has passed
  *            the call; calls that share a workspace must be ordered on a stream.
  *   workspace_bytes  its size in bytes.
  *   stream   hipStream_t (as void*); NULL for the null stream.

@@ -235,7 +235,7 @@ struct BwdParams {
   const __bf16* k;
   const __bf16* v;
   const __bf16* dO;
-  const float* lse;   // forward LSE, [BH, Nq]
+  const float* lse2;  // forward LSE times log2(e), [BH, Nq] (written by row_dot)
   const float* dd;    // D = rowsum(dO * O), [BH, Nq]
   void* dq;
   void* dk;
@@ -249,11 +249,13 @@ struct BwdParams {
 };
 
 // ---- D = rowsum(dO * O) --------------------------------------------------------------------
-// O is float32, or bf16 when o_bf16 is set; row r of D is (b*H + h)*Nq + i.
+// O is float32, or bf16 when o_bf16 is set; row r of D is (b*H + h)*Nq + i.  Also writes the
+// forward's LSE in log2 units, the form in which the gradient kernels use it.
 template <int D>
 __global__ __launch_bounds__(64) void row_dot_kernel(const __bf16* __restrict__ dO, Strides sdo,
                                                      const void* __restrict__ o, Strides so, int o_bf16,
-                                                     float* __restrict__ dd, int H, int Nq, int64_t rows) {
+                                                     const float* __restrict__ lse, float* __restrict__ dd,
+                                                     float* __restrict__ lse2, int H, int Nq, int64_t rows) {
   constexpr int TPR = D / 4, RPB = 64 / TPR;
   const int t = threadIdx.x % TPR;
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
@@ -275,7 +277,10 @@ __global__ __launch_bounds__(64) void row_dot_kernel(const __bf16* __restrict__ 
   }
 #pragma unroll
   for (int off = TPR / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, TPR);
-  if (row < rows && t == 0) dd[row] = s;
+  if (row < rows && t == 0) {
+    dd[row] = s;
+    lse2[row] = lse[row] * 1.4426950408889634f;  // log2 units, once per row instead of per score
+  }
 }
 
 // ---- dQ ------------------------------------------------------------------------------------
@@ -304,7 +309,7 @@ void dq_kernel(BwdParams p) {
   load_rows<D>(p.q + b * p.sq.b + h * p.sq.h, p.sq.n, my_row, Nq, hf, p.negate, qf);
   load_rows<D>(p.dO + b * p.sdo.b + h * p.sdo.h, p.sdo.n, my_row, Nq, hf, 0, dof);
   const int rc = my_row < Nq ? my_row : Nq - 1;
-  const float lse2 = p.lse[(int64_t)bh * Nq + rc] * 1.4426950408889634f;
+  const float lse2 = p.lse2[(int64_t)bh * Nq + rc];
   const float drow = p.dd[(int64_t)bh * Nq + rc];
   f32x16 acc[G::kDT];
 #pragma unroll
@@ -483,7 +488,7 @@ template <int I>
 __device__ __forceinline__ void score(const f32x16& s, const f32x16& dp, const f32x4 (&lv)[4], const f32x4 (&dvv)[4],
                                       float c_log2, Pending& cur) {
   const float sv = s[I];
-  const float l2 = lv[I >> 2][I & 3] * 1.4426950408889634f;
+  const float l2 = lv[I >> 2][I & 3];
   const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c_log2, -l2));
   cur.pb[I >> 3][I & 7] = (__bf16)pr;
   cur.dsb[I >> 3][I & 7] = (__bf16)(pr * (dp[I] - dvv[I >> 2][I & 3]));
@@ -569,7 +574,7 @@ void dkdv_kernel(BwdParams p) {
   const __bf16* qh = p.q + b * p.sq.b + h * p.sq.h;
   const __bf16* doh = p.dO + b * p.sdo.b + h * p.sdo.h;
   const unsigned qsb = (unsigned)(p.sq.n * 2), dosb = (unsigned)(p.sdo.n * 2);
-  const float* lh = p.lse + (int64_t)bh * Nq;
+  const float* lh = p.lse2 + (int64_t)bh * Nq;
   const float* dh = p.dd + (int64_t)bh * Nq;
   const unsigned base = (unsigned)(uintptr_t)(lds_void*)smem;
   // LDS: buffer u (0..2) holds Q at smem + 2u kTile, dO at smem + (2u + 1) kTile; the rows'
@@ -646,12 +651,13 @@ template <int D>
 constexpr int kDkdvLds = 6 * Geo<D>::kTile + kRowValsBytes;
 
 template <int D, bool CAUSAL>
-hipError_t launch_bwd(const BwdParams& p, const void* o, Strides so, int o_bf16, float* dd, hipStream_t s) {
+hipError_t launch_bwd(const BwdParams& p, const void* o, Strides so, int o_bf16, const float* lse, float* dd,
+                      float* lse2, hipStream_t s) {
   using G = Geo<D>;
   const int64_t rows = (int64_t)p.BH * p.Nq;
   constexpr int rpb = 64 / (D / 4);
   hipLaunchKernelGGL(row_dot_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(64), 0, s, p.dO, p.sdo, o, so,
-                     o_bf16, dd, p.H, p.Nq, rows);
+                     o_bf16, lse, dd, lse2, p.H, p.Nq, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   static const hipError_t a1 =
@@ -684,7 +690,7 @@ extern "C" __attribute__((visibility("hidden"))) void mifa_record_hip_error(int 
 
 extern "C" int64_t mifa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq) {
   if (B < 1 || H < 1 || Nq < 1 || B > ((int64_t)1 << 31) || H > ((int64_t)1 << 31)) return 0;
-  return B * H * Nq * 4;
+  return B * H * Nq * 8;  // D, then LSE in log2 units
 }
 
 namespace {
@@ -696,14 +702,16 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
             int o_bf16, int g_bf16, int causal, float scale, void* workspace, int64_t workspace_bytes,
             void* stream) {
   const int64_t BH = B * H;
-  if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes < BH * Nq * 4) return MIFA_ERR_WORKSPACE;
+  if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes < BH * Nq * 8) return MIFA_ERR_WORKSPACE;
   BwdParams p;
   p.q = (const __bf16*)q;
   p.k = (const __bf16*)k;
   p.v = (const __bf16*)v;
   p.dO = (const __bf16*)dO;
-  p.lse = lse;
-  p.dd = (const float*)workspace;
+  float* dd = (float*)workspace;
+  float* lse2 = dd + BH * Nq;
+  p.lse2 = lse2;
+  p.dd = dd;
   p.dq = dq;
   p.dk = dk;
   p.dv = dv;
@@ -726,12 +734,13 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const fl
   p.c_log2 = (float)c_exact;
   p.scale = scale;
   hipStream_t s = (hipStream_t)stream;
-  float* dd = (float*)workspace;
   hipError_t e;
   if (d == 128)
-    e = causal ? launch_bwd<128, true>(p, o, so, o_bf16, dd, s) : launch_bwd<128, false>(p, o, so, o_bf16, dd, s);
+    e = causal ? launch_bwd<128, true>(p, o, so, o_bf16, lse, dd, lse2, s)
+               : launch_bwd<128, false>(p, o, so, o_bf16, lse, dd, lse2, s);
   else
-    e = causal ? launch_bwd<64, true>(p, o, so, o_bf16, dd, s) : launch_bwd<64, false>(p, o, so, o_bf16, dd, s);
+    e = causal ? launch_bwd<64, true>(p, o, so, o_bf16, lse, dd, lse2, s)
+               : launch_bwd<64, false>(p, o, so, o_bf16, lse, dd, lse2, s);
   if (e != hipSuccess) {
     mifa_record_hip_error((int)e);
     return MIFA_ERR_HIP;

@@ -210,7 +210,7 @@ def _bwd(lib, q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, B=1, H=2, Nq=10
         (dict(do=A + 8), 4), (dict(dk=A + 4), 4), (dict(o=A + 2), 4), (dict(lse=A + 2), 4),
         (dict(scale=float("inf")), 5),
         (dict(Nq=1 << 24, Nk=1 << 24), 6),
-        (dict(ws=0), 9), (dict(ws=A + 8), 9), (dict(wsb=2 * 100 * 4 - 1), 9),
+        (dict(ws=0), 9), (dict(ws=A + 8), 9), (dict(wsb=2 * 100 * 8 - 1), 9),
     ],
 )
 def test_bwd_validation(lib, kw, status):
@@ -228,7 +228,7 @@ def test_bwd_validation_order(lib):
 
 def test_bwd_workspace_bytes(lib):
     assert lib.mifa_bwd_workspace_bytes(0, 1, 1) == 0
-    assert lib.mifa_bwd_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 4
+    assert lib.mifa_bwd_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 8
 
 
 # ---- the strided entry points ----------------------------------------------------------------

@@ -654,21 +654,18 @@ template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdParams& p, const void* o, Strides so, int o_bf16, const float* lse, float* dd,
                       float* lse2, hipStream_t s) {
   using G = Geo<D>;
+  hipError_t e;
+  // dynamic-LDS limits first, so that a failure leaves nothing half launched
+  static std::atomic<unsigned long long> done_dq4{0}, done_dq8{0}, done_dkdv{0};
+  if ((e = raise_lds_limit((const void*)dq_kernel<D, CAUSAL, 4>, G::kLds, done_dq4)) != hipSuccess) return e;
+  if ((e = raise_lds_limit((const void*)dq_kernel<D, CAUSAL, 8>, G::kLds, done_dq8)) != hipSuccess) return e;
+  if ((e = raise_lds_limit((const void*)dkdv_kernel<D, CAUSAL>, kDkdvLds<D>, done_dkdv)) != hipSuccess) return e;
   const int64_t rows = (int64_t)p.BH * p.Nq;
   constexpr int rpb = 64 / (D / 4);
   hipLaunchKernelGGL(row_dot_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(64), 0, s, p.dO, p.sdo, o, so,
                      o_bf16, lse, dd, lse2, p.H, p.Nq, rows);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  static const hipError_t a1 =
-      hipFuncSetAttribute((const void*)dq_kernel<D, CAUSAL, 4>, hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
-  static const hipError_t a3 =
-      hipFuncSetAttribute((const void*)dq_kernel<D, CAUSAL, 8>, hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
-  static const hipError_t a2 = hipFuncSetAttribute((const void*)dkdv_kernel<D, CAUSAL>,
-                                                   hipFuncAttributeMaxDynamicSharedMemorySize, kDkdvLds<D>);
-  if (a1 != hipSuccess) return a1;
-  if (a3 != hipSuccess) return a3;
-  if (a2 != hipSuccess) return a2;
   // 8-wave dq workgroups for long sequences with at least one such workgroup per CU
   const int64_t big_q = (int64_t)p.BH * ((p.Nq + 255) / 256);
   const bool dq8 = p.Nq > 4096 && big_q >= 256;

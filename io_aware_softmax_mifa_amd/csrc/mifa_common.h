@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <utility>
 
 namespace mifa_detail {
@@ -97,6 +98,21 @@ __device__ __forceinline__ float half_sum(float x) {
   float a, b;
   swap_halves(x, a, b);
   return a + b;
+}
+
+// ---- host: the dynamic-LDS limit of a kernel ----------------------------------------------------
+// Kernels that use more than the default dynamic LDS need the limit raised once on every device
+// they run on; `done` (one per kernel) records the devices already set.  Thread-safe: two
+// threads may both set it, which is harmless.
+inline hipError_t raise_lds_limit(const void* fn, int bytes, std::atomic<unsigned long long>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = dev >= 0 && dev < 64 ? (1ull << dev) : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
 }
 
 }  // namespace mifa_detail

@@ -636,9 +636,9 @@ hipError_t launch(const Problem& pr, hipStream_t stream) {
   p.lse_split = pr.lse_split;
   const int64_t grid = (int64_t)pr.BH * p.n_qtiles * pr.n_splits;
   auto kern = mifa_fwd_kernel<C, CAUSAL>;
-  // Raise the dynamic-LDS limit once per instantiation (thread-safe static initialisation).
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, C::kLdsBytes);
+  // Raise the dynamic-LDS limit once per instantiation and device.
+  static std::atomic<unsigned long long> done{0};
+  const hipError_t attr = raise_lds_limit((const void*)kern, C::kLdsBytes, done);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::kThreads), C::kLdsBytes, stream, p);
   return hipGetLastError();

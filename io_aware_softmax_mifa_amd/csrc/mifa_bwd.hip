@@ -383,10 +383,33 @@ void dq_kernel(BwdParams p) {
 template <int N>
 constexpr int kClampLgkm = N < 15 ? N : 15;
 
+// The lane-dependent part of every LDS address of the dV/dK kernel, computed once: the
+// row-major reads of row l%32 (one register per d slice) and the transposed reads (one per d
+// tile and half), both for tile 0.  Each block moves them to its buffer with one add per
+// register; the Q/dO tile, the 32-row tile and the contraction slice go into the instructions'
+// immediate offsets (the swizzles depend on the row mod 16 only, so those displacements are
+// plain byte offsets, and within one buffer they fit the 16-bit field).
 template <int D>
-__device__ __forceinline__ void issue_rows(unsigned tile, int row, int hf, bf16x8 (&a)[D / 16]) {
+struct LaneAddrs {
+  unsigned row[D / 16];
+  unsigned tr[D / 32][2];
+  __device__ __forceinline__ void init(unsigned base, int lane) {
+    const int ln = lane & 31, hf = lane >> 5;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) a[s] = lds_read_b128<0>(row_addr<D>(tile, row, s, hf));
+    for (int s = 0; s < D / 16; ++s) row[s] = row_addr<D>(base, ln, s, hf);
+    tr_addrs<D>(base, lane, tr);
+  }
+  __device__ __forceinline__ void shift(const LaneAddrs& a, unsigned by) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) row[s] = a.row[s] + by;
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) tr[t][0] = a.tr[t][0] + by, tr[t][1] = a.tr[t][1] + by;
+  }
+};
+template <int D, int OFF>
+__device__ __forceinline__ void issue_rows(const unsigned (&ra)[D / 16], bf16x8 (&a)[D / 16]) {
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) a[s] = lds_read_b128<OFF>(ra[s]);
 }
 // acc = sum_s a[s] (x) f[s]; AFTER reads were issued after a[] (their order is a, then those).
 template <int D, int AFTER, int S>
@@ -404,8 +427,9 @@ __device__ __forceinline__ void rows_product(bf16x8 (&a)[D / 16], const bf16x8 (
 template <int D, int KS>
 struct TrReads {
   i16x4 lo[D / 32], hi[D / 32];
+  template <int BOFF>
   __device__ __forceinline__ void issue(const unsigned (&tra)[D / 32][2]) {
-    constexpr int off = KS * 16 * D * 2;
+    constexpr int off = BOFF + KS * 16 * D * 2;
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
       lo[t] = lds_read_tr<off>(tra[t][0]);
@@ -424,14 +448,10 @@ struct TrReads {
   }
 };
 
-__device__ __forceinline__ f32x4 lds_read_f32x4_at(unsigned addr) {
+template <int OFF>
+__device__ __forceinline__ f32x4 lds_read_f32x4(unsigned addr) {
   f32x4 r;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr));
-  return r;
-}
-__device__ __forceinline__ f32x4 lds_read_f32x4_at256(unsigned addr) {
-  f32x4 r;
-  asm volatile("ds_read_b128 %0, %1 offset:256" : "=v"(r) : "v"(addr));
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
   return r;
 }
 
@@ -444,8 +464,9 @@ struct Pending {
   bf16x8 pb[2], dsb[2];
 };
 
-// The deferred products of tile TT, whose dO^T and Q^T operands sit in the tile pair at
-// do_base / q_base: dV^T += dO^T P, dK^T += Q^T dS, interleaved with this step's scores.
+// The deferred products of tile TT, whose dO^T and Q^T operands sit at byte offsets DO_OFF /
+// Q_OFF from the addresses tra_do / tra_q: dV^T += dO^T P, dK^T += Q^T dS, interleaved with
+// this step's scores.
 // The transposed reads go out first (after the current tile's row reads have all landed);
 // MFMA m of the 4 kDT waits for its own pair.
 template <int D, int TT>
@@ -453,11 +474,12 @@ struct DeferredReads {
   static constexpr int kDT = D / 32, kReads = 8 * kDT;
   TrReads<D, 2 * TT> do0, q0;
   TrReads<D, 2 * TT + 1> do1, q1;
+  template <int DO_OFF, int Q_OFF>
   __device__ __forceinline__ void issue(const unsigned (&tra_do)[kDT][2], const unsigned (&tra_q)[kDT][2]) {
-    do0.issue(tra_do);
-    do1.issue(tra_do);
-    q0.issue(tra_q);
-    q1.issue(tra_q);
+    do0.template issue<DO_OFF>(tra_do);
+    do1.template issue<DO_OFF>(tra_do);
+    q0.template issue<Q_OFF>(tra_q);
+    q1.template issue<Q_OFF>(tra_q);
   }
   template <int M>
   __device__ __forceinline__ void mfma_m(const Pending& pd, f32x16 (&dv)[kDT], f32x16 (&dk)[kDT]) {
@@ -495,27 +517,25 @@ __device__ __forceinline__ void score(const f32x16& s, const f32x16& dp, const f
 }
 
 // One 32-query tile TT of a query block: S = Q K^T and dP = dO V^T for the wave's 32 keys; then
-// the previous tile's dV/dK products (operands at ptra_do / ptra_q, its P and dS in prev)
-// interleaved with this tile's P and dS (into cur).
+// the previous tile's dV/dK products (its P and dS in prev) interleaved with this tile's P and dS
+// (into cur).  `at` addresses the block's buffer pair (Q, then dO one tile up), `pat` the buffer
+// pair of the previous tile; rvr the block's LSE and D rows.
 template <int D, bool CAUSAL, int TT>
-__device__ __forceinline__ void step(bool masked, unsigned qt_base, unsigned dot_base, unsigned rv, int ln, int hf,
-                                     const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16], int q0, int Nq,
-                                     int my_key, int kshift, float c_log2, const unsigned (&ptra_do)[D / 32][2],
-                                     const unsigned (&ptra_q)[D / 32][2], const Pending& prev, Pending& cur,
+__device__ __forceinline__ void step(bool masked, const LaneAddrs<D>& at, const LaneAddrs<D>& pat, unsigned rvr,
+                                     int hf, const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16], int q0, int Nq,
+                                     int my_key, int kshift, float c_log2, const Pending& prev, Pending& cur,
                                      f32x16 (&dv)[D / 32], f32x16 (&dk)[D / 32]) {
-  constexpr int kDS = D / 16, kNM = 4 * (D / 32);
+  constexpr int kDS = D / 16, kNM = 4 * (D / 32), kRowOff = 32 * TT * D * 2, kTile = Geo<D>::kTile;
   f32x4 lv[4], dvv[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    const unsigned ra = rv + (32 * TT + 8 * g + 4 * hf) * 4;
-    lv[g] = lds_read_f32x4_at(ra);
-    dvv[g] = lds_read_f32x4_at256(ra);
-  }
+  [&]<int... G>(std::integer_sequence<int, G...>) {
+    ((lv[G] = lds_read_f32x4<(32 * TT + 8 * G) * 4>(rvr), dvv[G] = lds_read_f32x4<256 + (32 * TT + 8 * G) * 4>(rvr)),
+     ...);
+  }(std::make_integer_sequence<int, 4>{});
   f32x16 s, dp;
   {
     bf16x8 qa[kDS], oa[kDS];
-    issue_rows<D>(qt_base, 32 * TT + ln, hf, qa);
-    issue_rows<D>(dot_base, 32 * TT + ln, hf, oa);
+    issue_rows<D, kRowOff>(at.row, qa);
+    issue_rows<D, kTile + kRowOff>(at.row, oa);
     rows_product<D, kDS>(qa, kf, s);
     rows_product<D, 0>(oa, vf, dp);
   }
@@ -532,7 +552,7 @@ __device__ __forceinline__ void step(bool masked, unsigned qt_base, unsigned dot
     }
   }
   DeferredReads<D, 1 - TT> pr;
-  pr.issue(ptra_do, ptra_q);
+  pr.template issue<kTile, 0>(pat.tr, pat.tr);
   [&]<int... I>(std::integer_sequence<int, I...>) {
     ((([&] {
         if constexpr ((I * kNM) % 16 == 0) pr.template mfma_m<I * kNM / 16>(prev, dv, dk);
@@ -602,7 +622,11 @@ void dkdv_kernel(BwdParams p) {
   Pending pend0, pend1;  // tile 0 / tile 1 of the latest block
 #pragma unroll
   for (int i = 0; i < 2; ++i) pend1.pb[i] = pend1.dsb[i] = (bf16x8){};
-  int pbuf = 2;          // buffer of the tile pending in pend1
+  LaneAddrs<D> lo;
+  lo.init(base, lane);
+  const unsigned rv0 = base + 6 * G::kTile + 16 * hf;
+  const float c = p.c_log2;
+  int pbuf = 2;  // buffer of the tile pending in pend1 (the zeroed one before the first block)
   if (jb < n_qb) load_block(jb, 0);
   for (int jq = jb; jq < n_qb; ++jq) {
     wait_vmcnt<0>();
@@ -610,31 +634,22 @@ void dkdv_kernel(BwdParams p) {
     __builtin_amdgcn_s_barrier();  // block jq has landed; buffer (jq+1) mod 3 was last read two steps ago
     const int u = (jq - jb) % 3;
     if (jq + 1 < n_qb) load_block(jq + 1, u == 2 ? 0 : u + 1);
-    const unsigned qt_base = base + 2 * u * G::kTile, dot_base = qt_base + G::kTile;
-    const unsigned pq_base = base + 2 * pbuf * G::kTile, pdo_base = pq_base + G::kTile;
-    const unsigned rv = base + 6 * G::kTile + u * 512;
+    LaneAddrs<D> at, pat;
+    at.shift(lo, (unsigned)(2 * u * G::kTile));
+    pat.shift(lo, (unsigned)(2 * pbuf * G::kTile));
+    const unsigned rvr = rv0 + u * 512;
     const int q0 = jq * kBlk;
     const bool masked = (CAUSAL && q0 + kshift < tile_key0 + kRows - 1) || q0 + kBlk > Nq;
-    unsigned tra_do[G::kDT][2], tra_q[G::kDT][2], ptra_do[G::kDT][2], ptra_q[G::kDT][2];
-    tr_addrs<D>(dot_base, lane, tra_do);
-    tr_addrs<D>(qt_base, lane, tra_q);
-    tr_addrs<D>(pdo_base, lane, ptra_do);
-    tr_addrs<D>(pq_base, lane, ptra_q);
-    const float c = p.c_log2;
-    step<D, CAUSAL, 0>(masked, qt_base, dot_base, rv, ln, hf, kf, vf, q0, Nq, my_key, kshift, c, ptra_do, ptra_q,
-                       pend1, pend0, dv, dk);
-    step<D, CAUSAL, 1>(masked, qt_base, dot_base, rv, ln, hf, kf, vf, q0, Nq, my_key, kshift, c, tra_do, tra_q,
-                       pend0, pend1, dv, dk);
+    step<D, CAUSAL, 0>(masked, at, pat, rvr, hf, kf, vf, q0, Nq, my_key, kshift, c, pend1, pend0, dv, dk);
+    step<D, CAUSAL, 1>(masked, at, at, rvr, hf, kf, vf, q0, Nq, my_key, kshift, c, pend0, pend1, dv, dk);
     pbuf = u;
   }
   // the last tile's dV/dK products
   {
-    const unsigned pq_base = base + 2 * pbuf * G::kTile, pdo_base = pq_base + G::kTile;
-    unsigned ptra_do[G::kDT][2], ptra_q[G::kDT][2];
-    tr_addrs<D>(pdo_base, lane, ptra_do);
-    tr_addrs<D>(pq_base, lane, ptra_q);
+    LaneAddrs<D> pat;
+    pat.shift(lo, (unsigned)(2 * pbuf * G::kTile));
     DeferredReads<D, 1> pr;
-    pr.issue(ptra_do, ptra_q);
+    pr.template issue<G::kTile, 0>(pat.tr, pat.tr);
     [&]<int... M>(std::integer_sequence<int, M...>) { (pr.template mfma_m<M>(pend1, dv, dk), ...); }(
         std::make_integer_sequence<int, 4 * G::kDT>{});
   }

@@ -18,8 +18,9 @@
 //  * dkdv: one workgroup per (b*h, 128-key tile), the roles swapped: each wave keeps 32 keys
 //    of K and V in registers, streams Q and dO blocks of 64 queries (with their LSE and D,
 //    three buffers), computes S = Q K^T and dP = dO V^T, then P and dS, and accumulates
-//    dV^T += dO^T P and dK^T += Q^T dS, each 32-query tile's products running during the next
-//    tile's score arithmetic.
+//    dV^T += dO^T P and dK^T += Q^T dS.  Software-pipelined: the score arithmetic of one
+//    32-query tile runs beside the S and dP products of the next and the dV/dK products of
+//    the previous one.
 // In both, the probabilities / dS feed the second product straight from the accumulator
 // layout (the contraction index inside one MFMA is a free permutation), as in the forward.
 #include <hip/hip_runtime.h>
@@ -516,33 +517,69 @@ __device__ __forceinline__ void score(const f32x16& s, const f32x16& dp, const f
   cur.dsb[I >> 3][I & 7] = (__bf16)(pr * (dp[I] - dvv[I >> 2][I & 3]));
 }
 
-// One 32-query tile TT of a query block: S = Q K^T and dP = dO V^T for the wave's 32 keys; then
-// the previous tile's dV/dK products (its P and dS in prev) interleaved with this tile's P and dS
-// (into cur).  `at` addresses the block's buffer pair (Q, then dO one tile up), `pat` the buffer
-// pair of the previous tile; rvr the block's LSE and D rows.
+// Scores I0 .. I0 + N - 1.
+template <int I0, int N>
+__device__ __forceinline__ void scores(const f32x16& s, const f32x16& dp, const f32x4 (&lv)[4], const f32x4 (&dvv)[4],
+                                       float c_log2, Pending& cur) {
+  if constexpr (N > 0) {
+    score<I0>(s, dp, lv, dvv, c_log2, cur);
+    scores<I0 + 1, N - 1>(s, dp, lv, dvv, c_log2, cur);
+  }
+}
+
+// ---- the software-pipelined step ----------------------------------------------------------
+// Step g (query tile g, 32 rows) runs three things at once: the softmax arithmetic of tile g (its
+// S and dP were computed in step g - 1), the S = Q K^T and dP = dO V^T chains of tile g + 1, and
+// the dV/dK products of tile g - 1.  Both product sets go to the MFMA pipe between the scores,
+// so the pipe has independent work while the VALU turns S and dP into P and dS.  With D/8 chain
+// MFMAs and D/8 deferred MFMAs per step, step g pairs chain MFMA i with deferred MFMA i; the
+// operands of pair i are one row-major read and two transposed reads, issued kLookahead pairs
+// ahead of their use.
+constexpr int kLookahead = 4;
+
+struct PairOps {
+  bf16x8 c;
+  i16x4 lo, hi;
+};
+// Operands of pair I: chain MFMA I reads slice I of the next tile's Q rows (I < D/16), then of
+// its dO rows; deferred MFMA I (d tile t = I mod D/32, part I / (D/32)) reads dO^T (parts 0, 1)
+// or Q^T (parts 2, 3) of the previous tile, contraction slice 2 TTP + part mod 2.
+template <int D, int TTN, int TTP, int I>
+__device__ __forceinline__ void issue_pair(const LaneAddrs<D>& nat, const LaneAddrs<D>& pat, PairOps& o) {
+  constexpr int kDS = D / 16, kDT = D / 32, kTile = Geo<D>::kTile, kRowOff = 32 * TTN * D * 2;
+  if constexpr (I < kDS)
+    o.c = lds_read_b128<kRowOff>(nat.row[I]);
+  else
+    o.c = lds_read_b128<kTile + kRowOff>(nat.row[I - kDS]);
+  constexpr int t = I % kDT, part = I / kDT;
+  constexpr int off = (part < 2 ? kTile : 0) + (2 * TTP + (part & 1)) * 16 * D * 2;
+  o.lo = lds_read_tr<off>(pat.tr[t][0]);
+  o.hi = lds_read_tr<off>(pat.tr[t][1]);
+}
+
+// Step TT (0 or 1) of a query block: scores of this block's tile TT from s_in / dp_in (P and dS
+// into cur; rows' LSE and D at rvr); chains of the next tile (its Q rows at nat, dO one tile up)
+// into s_out / dp_out; dV/dK products of the previous tile (P and dS in prev, Q^T at pat, dO^T
+// one tile up).  The next and the previous tile both sit at position 1 - TT of their blocks.
 template <int D, bool CAUSAL, int TT>
-__device__ __forceinline__ void step(bool masked, const LaneAddrs<D>& at, const LaneAddrs<D>& pat, unsigned rvr,
+__device__ __forceinline__ void step(bool masked, const LaneAddrs<D>& nat, const LaneAddrs<D>& pat, unsigned rvr,
                                      int hf, const bf16x8 (&kf)[D / 16], const bf16x8 (&vf)[D / 16], int q0, int Nq,
                                      int my_key, int kshift, float c_log2, const Pending& prev, Pending& cur,
+                                     const f32x16& s_in, const f32x16& dp_in, f32x16& s_out, f32x16& dp_out,
                                      f32x16 (&dv)[D / 32], f32x16 (&dk)[D / 32]) {
-  constexpr int kDS = D / 16, kNM = 4 * (D / 32), kRowOff = 32 * TT * D * 2, kTile = Geo<D>::kTile;
+  constexpr int kDS = D / 16, kDT = D / 32, kNP = D / 8, kSPP = 16 / kNP;
+  constexpr int kTTN = 1 - TT, kTTP = 1 - TT;
   f32x4 lv[4], dvv[4];
   [&]<int... G>(std::integer_sequence<int, G...>) {
     ((lv[G] = lds_read_f32x4<(32 * TT + 8 * G) * 4>(rvr), dvv[G] = lds_read_f32x4<256 + (32 * TT + 8 * G) * 4>(rvr)),
      ...);
   }(std::make_integer_sequence<int, 4>{});
-  f32x16 s, dp;
-  {
-    bf16x8 qa[kDS], oa[kDS];
-    issue_rows<D, kRowOff>(at.row, qa);
-    issue_rows<D, kTile + kRowOff>(at.row, oa);
-    rows_product<D, kDS>(qa, kf, s);
-    rows_product<D, 0>(oa, vf, dp);
-  }
-  // every read issued so far has landed (the last wait above counted none outstanding)
-#pragma unroll
-  for (int g = 0; g < 4; ++g) asm volatile("" : "+v"(lv[g]), "+v"(dvv[g]));
+  PairOps ops[kNP];
+  [&]<int... P>(std::integer_sequence<int, P...>) {
+    (issue_pair<D, kTTN, kTTP, P>(nat, pat, ops[P]), ...);
+  }(std::make_integer_sequence<int, (kLookahead < kNP ? kLookahead : kNP)>{});
   // Blocks on the causal diagonal or past the last query: hidden scores get -inf (P = 0).
+  f32x16 s = s_in;
   if (masked) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -551,15 +588,44 @@ __device__ __forceinline__ void step(bool masked, const LaneAddrs<D>& at, const 
       s[i] = vis ? s[i] : -__builtin_inff();
     }
   }
-  DeferredReads<D, 1 - TT> pr;
-  pr.template issue<kTile, 0>(pat.tr, pat.tr);
+  auto op = [](const i16x4& lo, const i16x4& hi) {
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   [&]<int... I>(std::integer_sequence<int, I...>) {
-    ((([&] {
-        if constexpr ((I * kNM) % 16 == 0) pr.template mfma_m<I * kNM / 16>(prev, dv, dk);
-      }()),
-      score<I>(s, dp, lv, dvv, c_log2, cur)),
+    (([&] {
+       if constexpr (I + kLookahead < kNP) issue_pair<D, kTTN, kTTP, I + kLookahead>(nat, pat, ops[I + kLookahead]);
+       // LDS reads complete in order: count the reads issued after the one needed
+       constexpr int issued = I + kLookahead + 1 < kNP ? I + kLookahead + 1 : kNP;
+       lgkm_wait<kClampLgkm<3 * (issued - I - 1) + 2>>(ops[I].c);
+       if constexpr (I == 0) {
+         // the row values went out before every pair: they have landed
+#pragma unroll
+         for (int g = 0; g < 4; ++g) asm volatile("" : "+v"(lv[g]), "+v"(dvv[g]));
+       }
+       if constexpr (I < kDS)
+         s_out = mfma(ops[I].c, kf[I], I == 0 ? (f32x16){} : s_out);
+       else
+         dp_out = mfma(ops[I].c, vf[I - kDS], I == kDS ? (f32x16){} : dp_out);
+       scores<I * kSPP, kSPP>(s, dp_in, lv, dvv, c_log2, cur);
+       // Keep the scores in this pair: their only users are the next step's MFMAs, and without
+       // the tie they would sink past the barrier that follows the step.
+       if constexpr (((I + 1) * kSPP) % 2 == 0) {
+         constexpr int v = ((I + 1) * kSPP - 1) >> 3;
+         asm volatile("" : "+v"(cur.pb[v]), "+v"(cur.dsb[v]));
+       }
+       lgkm_wait<kClampLgkm<3 * (issued - I - 1)>>(ops[I].lo, ops[I].hi);
+       constexpr int t = I % kDT, part = I / kDT;
+       if constexpr (part == 0)
+         dv[t] = mfma(op(ops[I].lo, ops[I].hi), prev.pb[0], dv[t]);
+       else if constexpr (part == 1)
+         dv[t] = mfma(op(ops[I].lo, ops[I].hi), prev.pb[1], dv[t]);
+       else if constexpr (part == 2)
+         dk[t] = mfma(op(ops[I].lo, ops[I].hi), prev.dsb[0], dk[t]);
+       else
+         dk[t] = mfma(op(ops[I].lo, ops[I].hi), prev.dsb[1], dk[t]);
+     }()),
      ...);
-  }(std::make_integer_sequence<int, 16>{});
+  }(std::make_integer_sequence<int, kNP>{});
 }
 
 template <int D, bool CAUSAL>
@@ -604,12 +670,13 @@ void dkdv_kernel(BwdParams p) {
     const int limit = Nq - 1 - jq * kBlk;
     dma_tile<D>(qh + (int64_t)jq * kBlk * p.sq.n, smem + 2 * buf * G::kTile, wave, lane, limit, qsb);
     dma_tile<D>(doh + (int64_t)jq * kBlk * p.sdo.n, smem + (2 * buf + 1) * G::kTile, wave, lane, limit, dosb);
-    if (wave == 0) {
+    // The rows' LSE (wave 1) and D (wave 2): a load instruction costs the issuing wave tens of
+    // cycles, and every wave waits for the slowest at the next barrier.
+    if (wave == 1 || wave == 2) {
       const int r = lane < limit ? lane : limit;
-      __builtin_amdgcn_global_load_lds((global_cvoid*)(lh + (int64_t)jq * kBlk + r), (lds_void*)(rowvals + buf * 512),
-                                       4, 0, 0);
-      __builtin_amdgcn_global_load_lds((global_cvoid*)(dh + (int64_t)jq * kBlk + r),
-                                       (lds_void*)(rowvals + buf * 512 + 256), 4, 0, 0);
+      const float* src = (wave == 1 ? lh : dh) + (int64_t)jq * kBlk + r;
+      __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)(rowvals + buf * 512 + (wave - 1) * 256), 4, 0,
+                                       0);
     }
   };
   // The first step's deferred products read buffer 2 with P = dS = 0; zero it so that those
@@ -626,22 +693,44 @@ void dkdv_kernel(BwdParams p) {
   lo.init(base, lane);
   const unsigned rv0 = base + 6 * G::kTile + 16 * hf;
   const float c = p.c_log2;
-  int pbuf = 2;  // buffer of the tile pending in pend1 (the zeroed one before the first block)
-  if (jb < n_qb) load_block(jb, 0);
-  for (int jq = jb; jq < n_qb; ++jq) {
+  // S and dP of the tile whose scores the next step computes: [0] for a block's first tile,
+  // [1] for its second.
+  f32x16 sa[2], dpa[2];
+  if (jb < n_qb) {
+    load_block(jb, 0);
+    if (jb + 1 < n_qb) load_block(jb + 1, 1);
     wait_vmcnt<0>();
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // block jq has landed; buffer (jq+1) mod 3 was last read two steps ago
-    const int u = (jq - jb) % 3;
-    if (jq + 1 < n_qb) load_block(jq + 1, u == 2 ? 0 : u + 1);
+    __builtin_amdgcn_s_barrier();  // blocks jb, jb + 1 and the zeroed buffer 2 are in place
+    bf16x8 qa[G::kDS], oa[G::kDS];
+    issue_rows<D, 0>(lo.row, qa);
+    issue_rows<D, G::kTile>(lo.row, oa);
+    rows_product<D, G::kDS>(qa, kf, sa[0]);
+    rows_product<D, 0>(oa, vf, dpa[0]);
+  }
+  // Block jb + i sits in buffer i mod 3.  Step 0 of block jq reads its own buffer and the
+  // previous block's; step 1 reads its own and the next block's.  Between the two steps every
+  // wave has finished with the previous block, which is refilled with block jq + 2.
+  int pbuf = 2;  // buffer of the tile pending after the loop (the zeroed one if there was no block)
+  for (int jq = jb; jq < n_qb; ++jq) {
+    const int u = (jq - jb) % 3, un = u == 2 ? 0 : u + 1, up = u == 0 ? 2 : u - 1;
     LaneAddrs<D> at, pat;
     at.shift(lo, (unsigned)(2 * u * G::kTile));
-    pat.shift(lo, (unsigned)(2 * pbuf * G::kTile));
+    pat.shift(lo, (unsigned)(2 * up * G::kTile));
     const unsigned rvr = rv0 + u * 512;
     const int q0 = jq * kBlk;
     const bool masked = (CAUSAL && q0 + kshift < tile_key0 + kRows - 1) || q0 + kBlk > Nq;
-    step<D, CAUSAL, 0>(masked, at, pat, rvr, hf, kf, vf, q0, Nq, my_key, kshift, c, pend1, pend0, dv, dk);
-    step<D, CAUSAL, 1>(masked, at, at, rvr, hf, kf, vf, q0, Nq, my_key, kshift, c, pend0, pend1, dv, dk);
+    step<D, CAUSAL, 0>(masked, at, pat, rvr, hf, kf, vf, q0, Nq, my_key, kshift, c, pend1, pend0, sa[0], dpa[0], sa[1],
+                       dpa[1], dv, dk);
+    wait_vmcnt<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // block jq + 1 has landed; block jq - 1's buffer is free
+    if (jq + 2 < n_qb) load_block(jq + 2, up);
+    // After the last block the chains read a stale buffer; their S and dP are never used.
+    LaneAddrs<D> nat;
+    nat.shift(lo, (unsigned)(2 * un * G::kTile));
+    step<D, CAUSAL, 1>(masked, nat, at, rvr, hf, kf, vf, q0, Nq, my_key, kshift, c, pend0, pend1, sa[1], dpa[1], sa[0],
+                       dpa[0], dv, dk);
     pbuf = u;
   }
   // the last tile's dV/dK products

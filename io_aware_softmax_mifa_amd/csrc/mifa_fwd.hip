@@ -109,6 +109,7 @@ struct Lane {
   unsigned v[C::kDT];           // V^T operand of dv tile t, key slice 0, V buffer 0
   unsigned dk[C::kInstPerWave]; // DMA source byte offsets within a key block (K)
   unsigned dv[C::kInstPerWave]; // (V)
+  unsigned pdk[C::kInstPerWave], pdv[C::kInstPerWave];  // the same for wave + WAVES/2
   unsigned ksb, vsb;            // K and V row strides in bytes (wave-uniform)
 };
 
@@ -148,24 +149,27 @@ __device__ __forceinline__ Lane<C> lane_setup(unsigned smem_base, int wave, int 
   a.ksb = ksb;
   a.vsb = vsb;
   dma_offsets<C>(a.dk, a.dv, wave, lane, C::BC, ksb, vsb);
+  dma_offsets<C>(a.pdk, a.pdv, wave + C::WAVES / 2, lane, C::BC, ksb, vsb);
   return a;
 }
 
-// Issue the DMA of K block kblk into K buffer kbuf and of V block vblk into V buffer vbuf.  Block
-// bases are wave-uniform, the per-lane parts 32-bit byte offsets.  Every call issues the same
-// number of DMA ops, so vector-memory waits can use fixed counts.
+// Issue wave `wave`'s share of the DMA of K block kblk into K buffer kbuf and of V block vblk
+// into V buffer vbuf (odk / odv: that share's per-lane source offsets).  Block bases are
+// wave-uniform, the per-lane parts 32-bit byte offsets.  Every call issues the same number of
+// DMA ops, so vector-memory waits can use fixed counts.
 template <typename C>
 __device__ __forceinline__ void issue_dma(const __bf16* __restrict__ kbase, const __bf16* __restrict__ vbase,
                                           char* smem, int kblk, int kbuf, int vblk, int vbuf, int N, int wave,
-                                          int lane, const Lane<C>& la) {
+                                          int lane, const Lane<C>& la, const unsigned (&odk)[C::kInstPerWave],
+                                          const unsigned (&odv)[C::kInstPerWave]) {
   constexpr int D = C::D, BC = C::BC;
   const char* kb = (const char*)kbase + (int64_t)kblk * BC * la.ksb;
   const char* vb = (const char*)vbase + (int64_t)vblk * BC * la.vsb;
   unsigned dk[C::kInstPerWave], dv[C::kInstPerWave], tk[C::kInstPerWave], tv[C::kInstPerWave];
 #pragma unroll
   for (int t = 0; t < C::kInstPerWave; ++t) {
-    dk[t] = la.dk[t];
-    dv[t] = la.dv[t];
+    dk[t] = odk[t];
+    dv[t] = odv[t];
   }
   // In the last, partial block, rows past N are clamped to N-1: they are masked out of the
   // softmax, and clamping keeps every global address inside the tensors.
@@ -183,6 +187,12 @@ __device__ __forceinline__ void issue_dma(const __bf16* __restrict__ kbase, cons
     __builtin_amdgcn_global_load_lds((global_cvoid*)(kb + dk[t]), (lds_void*)(kdst + inst * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((global_cvoid*)(vb + dv[t]), (lds_void*)(vdst + inst * 1024), 16, 0, 0);
   }
+}
+template <typename C>
+__device__ __forceinline__ void issue_dma(const __bf16* __restrict__ kbase, const __bf16* __restrict__ vbase,
+                                          char* smem, int kblk, int kbuf, int vblk, int vbuf, int N, int wave,
+                                          int lane, const Lane<C>& la) {
+  issue_dma<C>(kbase, vbase, smem, kblk, kbuf, vblk, vbuf, N, wave, lane, la, la.dk, la.dv);
 }
 
 // ---- the per-wave pipeline stages -------------------------------------------------------------
@@ -508,12 +518,22 @@ void mifa_fwd_kernel(FwdParams p) {
   if constexpr (NBUF == 4) {
     // ---- DMA schedule: one barrier per two blocks ----
     // K(i) lives in K buffer i % 4 and V(i) in V buffer i % 4.  Before every even block j all
-    // waves meet at a barrier, and right after it each wave issues its share of K(j+3), K(j+4),
-    // V(j+2), V(j+3): the buffers blocks j-2 and j-1 have released.  Blocks j and j+1 read
-    // K(j+1), K(j+2), V(j), V(j+1), all issued at the previous even barrier and waited for
-    // (vmcnt 0) before this one.  Between barriers the waves drift up to a block apart.
+    // waves meet at a barrier, and right after it the DMA of K(j+3), K(j+4), V(j+2), V(j+3)
+    // goes out: the buffers blocks j-2 and j-1 have released.  Blocks j and j+1 read K(j+1),
+    // K(j+2), V(j), V(j+1), all issued at the previous even barrier and waited for (vmcnt 0)
+    // before this one.  Between barriers the waves drift up to a block apart.
+    //   A load instruction holds up its wave for tens of cycles.  Inside the loop only the
+    // high-priority waves issue, each its own share and that of the wave it shares a SIMD with:
+    // they run ahead and would wait at the next barrier anyway, and while they issue, the other
+    // wave of the SIMD keeps the matrix unit busy.
     auto pair = [&](int kb, int vb) {
       issue_dma<C>(kh, vh, smem, min(kb, last), kb % NBUF, min(vb, last), vb % NBUF, N, wave, lane, W.la);
+    };
+    auto pair2 = [&](int kb, int vb) {
+      issue_dma<C>(kh, vh, smem, min(kb, last), kb % NBUF, min(vb, last), vb % NBUF, N, wave, lane, W.la, W.la.dk,
+                   W.la.dv);
+      issue_dma<C>(kh, vh, smem, min(kb, last), kb % NBUF, min(vb, last), vb % NBUF, N, wave + C::WAVES / 2, lane,
+                   W.la, W.la.pdk, W.la.pdv);
     };
     pair(0, 0);
     pair(1, 1);
@@ -525,8 +545,10 @@ void mifa_fwd_kernel(FwdParams p) {
       if constexpr (U % 2 == 0) {
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
-        pair(j + 3, j + 2);
-        pair(j + 4, j + 3);
+        if (wave < C::WAVES / 2) {
+          pair2(j + 3, j + 2);
+          pair2(j + 4, j + 3);
+        }
       }
       W.template block<(U + 1) % NBUF, U % NBUF>(cur, nxt, j * BC, j >= j_mask);
     };

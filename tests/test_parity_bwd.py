@@ -90,6 +90,10 @@ SHAPES = [
     (1, 2, 333, 100, 64, False, 11),     # more queries than keys
     (2, 4, 1024, 1024, 128, True, 12),
     (1, 4, 1024, 1024, 64, False, 13),
+    (1, 2, 129, 129, 128, True, 14),     # last query block holds one row
+    (1, 2, 192, 192, 128, False, 15),    # exactly three blocks: each buffer of the ring once
+    (1, 2, 64, 64, 64, True, 16),        # exactly one block: the pipeline's prologue and epilogue only
+    (1, 1, 4096, 4096, 64, True, 17),    # up to 64 blocks per key tile: the ring wraps many times
 ]
 
 

@@ -208,13 +208,6 @@ __device__ __forceinline__ void transposed_products(const unsigned (&tra)[D / 32
   [&]<int... KS>(std::integer_sequence<int, KS...>) { (tp_step<D>(tra, pb, acc, KS, IC<KS>{}), ...); }(
       std::make_integer_sequence<int, 4>{});
 }
-// Slices 2 TT and 2 TT + 1 only (one 32-row tile of the contraction), pb holding those two.
-template <int D, int TT>
-__device__ __forceinline__ void transposed_products_tile(const unsigned (&tra)[D / 32][2], const bf16x8 (&pb)[2],
-                                                         f32x16 (&acc)[D / 32]) {
-  tp_step<D>(tra, pb, acc, 0, IC<2 * TT>{});
-  tp_step<D>(tra, pb, acc, 1, IC<2 * TT + 1>{});
-}
 
 template <int D>
 __device__ __forceinline__ void tr_addrs(unsigned tile, int lane, unsigned (&tra)[D / 32][2]) {
@@ -376,11 +369,10 @@ void dq_kernel(BwdParams p) {
 }
 
 // ---- dK, dV -------------------------------------------------------------------------------
-// At one wave per SIMD nothing else hides an LDS round trip, so the reads of each stage are
-// issued ahead of the MFMAs of the stage before: the row values (LSE, D) and the Q and dO rows
-// of a tile go out together, and the transposed operands of the four dV/dK steps run one step
-// ahead.  Waits count the reads issued after the one needed (LDS reads complete in order);
-// counts above the 4-bit field are clamped, which only waits longer.
+// At one wave per SIMD nothing else hides an LDS round trip, so every LDS read is issued ahead
+// of the MFMA that consumes it (see the pipelined step below).  Waits count the reads issued
+// after the one needed (LDS reads complete in order); counts above the 4-bit field are clamped,
+// which only waits longer.
 template <int N>
 constexpr int kClampLgkm = N < 15 ? N : 15;
 
@@ -437,16 +429,6 @@ struct TrReads {
       hi[t] = lds_read_tr<off>(tra[t][1]);
     }
   }
-  // acc[t] += tile^T slice KS (x) pb; AFTER reads were issued after these.
-  template <int AFTER>
-  __device__ __forceinline__ void mfmas(const bf16x8& pb, f32x16 (&acc)[D / 32]) {
-    [&]<int... T>(std::integer_sequence<int, T...>) {
-      ((lgkm_wait<kClampLgkm<AFTER + 2 * (D / 32 - 1 - T)>>(lo[T], hi[T]),
-        acc[T] = mfma(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo[T], hi[T], 0, 1, 2, 3, 4, 5, 6, 7)), pb,
-                      acc[T])),
-       ...);
-    }(std::make_integer_sequence<int, D / 32>{});
-  }
 };
 
 template <int OFF>
@@ -465,11 +447,10 @@ struct Pending {
   bf16x8 pb[2], dsb[2];
 };
 
-// The deferred products of tile TT, whose dO^T and Q^T operands sit at byte offsets DO_OFF /
-// Q_OFF from the addresses tra_do / tra_q: dV^T += dO^T P, dK^T += Q^T dS, interleaved with
-// this step's scores.
-// The transposed reads go out first (after the current tile's row reads have all landed);
-// MFMA m of the 4 kDT waits for its own pair.
+// The dV/dK products of tile TT of a block, all at once (the last tile's, after the loop):
+// dO^T and Q^T sit at byte offsets DO_OFF / Q_OFF from the addresses tra_do / tra_q;
+// dV^T += dO^T P, dK^T += Q^T dS.  All transposed reads go out first; MFMA m of the 4 kDT waits
+// for its own pair.
 template <int D, int TT>
 struct DeferredReads {
   static constexpr int kDT = D / 32, kReads = 8 * kDT;

@@ -30,9 +30,10 @@
 //    in-lane reductions plus one v_permlane32_swap with the other half of the wave.
 //  * Each wave is software-pipelined over key blocks: while its VALU runs the softmax of block
 //    j, its MFMAs compute the scores of block j+1 (K runs one block ahead of V in LDS), and
-//    then the PV product of block j follows.  K and V^T operands are read from LDS through
-//    small register rings with explicit waits, so the MFMA chains never stall on a read that
-//    could have been issued earlier.
+//    then the PV product of block j follows, one chunk of 16-key slices at a time as soon as
+//    that chunk's weights exist, beside the exponentials of the next chunk.  K and V^T operands
+//    are read from LDS through small register rings with explicit waits, so the MFMA chains
+//    never stall on a read that could have been issued earlier.
 //  * Softmax runs in the log2 domain (exp2 on v_exp_f32, with scale * log2(e) folded into one
 //    FMA per score).  The running max used for exponentiation is only raised when a block's
 //    max exceeds it by more than kRescaleSlack (2^8): the output and row sum are then
@@ -285,25 +286,33 @@ struct Wave {
   }
 
   // ---- softmax, part 2: P = exp2(S * c - m) packed to bf16, and the row sum ----
-  // A masked score is -inf and c > 0, so its weight is exp2(-inf) = 0.
-  __device__ __forceinline__ void softmax_exp(const f32x16 (&sacc)[C::kKT], bf16x8 (&pb)[C::kKS]) {
-    float ls4[4];
-    // A row that has seen no visible key yet (m = -inf; possible when the workgroup covers a
-    // key range that starts after the row's last key) must get weight exp2(-inf) = 0, not
-    // exp2(-inf + inf).
-    const float neg_m = m_run == -__builtin_inff() ? 0.f : -m_run;
+  // A masked score is -inf and c > 0, so its weight is exp2(-inf) = 0.  The weights are produced
+  // one 16-key slice at a time (slice ks -> pb[ks]), so that the PV steps of a slice can start
+  // while later slices are still being exponentiated.  ls4 collects the row sum in the same
+  // order whatever the chunking.
+  // A row that has seen no visible key yet (m = -inf; possible when the workgroup covers a key
+  // range that starts after the row's last key) must get weight exp2(-inf) = 0, not
+  // exp2(-inf + inf): neg_m is then 0.
+  __device__ __forceinline__ float neg_max() const { return m_run == -__builtin_inff() ? 0.f : -m_run; }
+  template <int KS>
+  __device__ __forceinline__ void softmax_exp_slice(const f32x16 (&sacc)[C::kKT], bf16x8 (&pb)[C::kKS], float neg_m,
+                                                    float (&ls4)[4]) {
+    constexpr int kt = KS / 2, i0 = 8 * (KS % 2);
 #pragma unroll
-    for (int kt = 0; kt < C::kKT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][i], c, neg_m));
-        if (kt == 0 && i < 4)
-          ls4[i] = p;
-        else
-          ls4[i & 3] += p;
-        pb[2 * kt + (i >> 3)][i & 7] = (__bf16)p;
-      }
-    l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
+    for (int i = i0; i < i0 + 8; ++i) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][i], c, neg_m));
+      if (KS == 0 && i < 4)
+        ls4[i] = p;
+      else
+        ls4[i & 3] += p;
+      pb[KS][i & 7] = (__bf16)p;
+    }
+  }
+  template <int K0, int K1>
+  __device__ __forceinline__ void softmax_exp_slices(const f32x16 (&sacc)[C::kKT], bf16x8 (&pb)[C::kKS], float neg_m,
+                                                     float (&ls4)[4]) {
+    [&]<int... K>(std::integer_sequence<int, K...>) { (softmax_exp_slice<K0 + K>(sacc, pb, neg_m, ls4), ...); }(
+        std::make_integer_sequence<int, K1 - K0>{});
   }
 
   // ---- O^T += V^T P^T for one block ----
@@ -337,18 +346,31 @@ struct Wave {
     // multiplied anyway, which keeps this path free of branches.)
     oacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16), pb[ks], oacc[t], 0, 0, 0);
   }
-  template <int VB>
-  __device__ __forceinline__ void pv(const bf16x8 (&pb)[C::kKS], i16x4 (&vr)[kVR]) {
-    [&]<int... St>(std::integer_sequence<int, St...>) { (pv_step<VB>(pb, vr, IC<St>{}), ...); }(
-        std::make_integer_sequence<int, C::kPVSteps>{});
+  // PV steps of key slices K0 .. K1-1.
+  template <int VB, int K0, int K1>
+  __device__ __forceinline__ void pv_slices(const bf16x8 (&pb)[C::kKS], i16x4 (&vr)[kVR]) {
+    [&]<int... St>(std::integer_sequence<int, St...>) { (pv_step<VB>(pb, vr, IC<K0 * C::kDT + St>{}), ...); }(
+        std::make_integer_sequence<int, (K1 - K0) * C::kDT>{});
   }
 
   // ---- one key block j, with the scores of block j+1 computed alongside ----
   // `cur` holds S^T(j) on entry and `nxt` holds S^T(j+1) on exit.  kbuf / vbuf are the byte
   // offsets of the buffers holding K(j+1) and V(j).  The first half of the S^T(j+1) MFMAs sits
-  // with the row max, the second half with the exponentials, so MFMA and VALU work interleave.
+  // with the row max, the second half with the first chunk of exponentials; the PV steps of each
+  // chunk of key slices then run beside the exponentials of the next chunk, so that no long
+  // stretch of the wave is all VALU or all MFMA.  Chunks of one slice suit the 8-wave kernel
+  // (one workgroup per CU), chunks of two the 4-wave kernel (two per CU), by measurement.
   // On the last block the K buffer holds no new block and the scores computed from it are
   // unused.
+  static constexpr int kExpChunk = C::WAVES == 8 ? 1 : 2;  // key slices per chunk
+  static_assert(C::kKS % kExpChunk == 0, "chunks tile the key slices");
+  template <int VB, int G>
+  __device__ __forceinline__ void pv_chunk(const f32x16 (&cur)[C::kKT], bf16x8 (&pb)[C::kKS], i16x4 (&vr)[kVR],
+                                           float neg_m, float (&ls4)[4]) {
+    constexpr int k0 = G * kExpChunk, k1 = k0 + kExpChunk;
+    pv_slices<VB, k0, k1>(pb, vr);
+    if constexpr (k1 < C::kKS) softmax_exp_slices<k1, k1 + kExpChunk>(cur, pb, neg_m, ls4);
+  }
   template <int KB, int VB>
   __device__ __forceinline__ void block(f32x16 (&cur)[C::kKT], f32x16 (&nxt)[C::kKT], int key0, bool masked) {
     bf16x8 kr[kKR];
@@ -361,10 +383,14 @@ struct Wave {
     if (__builtin_amdgcn_ballot_w64(grow)) rescale(grow, bm);
     bf16x8 pb[C::kKS];
     s_steps<KB, half, C::kSSteps>(nxt, kr);
-    softmax_exp(cur, pb);
+    const float neg_m = neg_max();
+    float ls4[4];
+    softmax_exp_slices<0, kExpChunk>(cur, pb, neg_m, ls4);
     i16x4 vr[kVR];
     pv_start<VB>(vr);
-    pv<VB>(pb, vr);
+    [&]<int... G>(std::integer_sequence<int, G...>) { (pv_chunk<VB, G>(cur, pb, vr, neg_m, ls4), ...); }(
+        std::make_integer_sequence<int, C::kKS / kExpChunk>{});
+    l_run += (ls4[0] + ls4[1]) + (ls4[2] + ls4[3]);
   }
 
   // Scores of the first block (no softmax to overlap with); K(0) is in K buffer 0.

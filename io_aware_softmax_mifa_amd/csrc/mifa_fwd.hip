@@ -46,7 +46,8 @@
 //    4 x 16 block of bf16 across each 16-lane group.  Each lane accumulates O for its own
 //    query, so the per-row rescale and the final 1/l are in-lane multiplies.
 //  * Only the blocks that straddle the causal diagonal or the end of the sequence run the
-//    masking code; all other blocks take a mask-free path.
+//    masking code; all other blocks take a mask-free path.  A wave stops computing after the
+//    last block any of its rows can see (it keeps joining the workgroup's barriers).
 //  * LDS tiles are XOR-swizzled in 16-byte chunks to spread the K reads and the V transpose
 //    reads over the banks.  The main loop is unrolled over the buffer ring, so every LDS read
 //    address is a per-lane register plus an immediate offset.
@@ -499,6 +500,17 @@ void mifa_fwd_kernel(FwdParams p) {
   W.row0 = qt * kBR + wave * kRowsPerWave;
   W.my_row = W.row0 + ln;
   W.my_pos = W.my_row + kshift - key_base;
+  // Key blocks this wave needs: with the causal mask, up to the last visible key of its last
+  // row (the blocks after that are fully masked for all its rows and would add exp2(-inf) = 0
+  // weights); none when all its rows lie past the end.  The wave still takes part in every
+  // barrier and DMA of the workgroup's longer loop.
+  int nblk_w = nblk;
+  if (CAUSAL) {
+    const int wave_last = min(Nq - 1, W.row0 + kRowsPerWave - 1);
+    nblk_w = min(nblk, min(n_kblocks, (wave_last + kshift) / BC + 1) - jb0);
+  }
+  if (W.row0 >= Nq) nblk_w = 0;
+  nblk_w = __builtin_amdgcn_readfirstlane(nblk_w);
   W.hf = hf;
   W.c = p.c_log2;
   W.m_run = -__builtin_inff();
@@ -576,7 +588,7 @@ void mifa_fwd_kernel(FwdParams p) {
           pair2(j + 4, j + 3);
         }
       }
-      W.template block<(U + 1) % NBUF, U % NBUF>(cur, nxt, j * BC, j >= j_mask);
+      if (j < nblk_w) W.template block<(U + 1) % NBUF, U % NBUF>(cur, nxt, j * BC, j >= j_mask);
     };
     for (int j0 = 0; j0 < nblk; j0 += C::kUnroll) {
       [&]<int... U>(std::integer_sequence<int, U...>) {
@@ -609,7 +621,7 @@ void mifa_fwd_kernel(FwdParams p) {
     wait_vmcnt<(NBUF - 2) * C::kDmaPerGroup>();  // K(j+1) and V(j) have landed
     __builtin_amdgcn_s_barrier();                // ... for every wave; block j-1 is done
     group(j);
-    W.template block<(U + 1) % NBUF, U % NBUF>(cur, nxt, j * BC, j >= j_mask);
+    if (j < nblk_w) W.template block<(U + 1) % NBUF, U % NBUF>(cur, nxt, j * BC, j >= j_mask);
   };
   for (int j0 = 0; j0 < nblk; j0 += C::kUnroll) {
     [&]<int... U>(std::integer_sequence<int, U...>) {

@@ -10,6 +10,9 @@ the timed region.  Prints ONE JSON line on stdout.
 
 FLOPs per step follow the usual attention convention: 4*B*H*N^2*d, halved for causal.
 
+Warm-up: --warmup W runs exactly W untimed launches; without it, at least 30 launches and at
+least 0.5 s of them, and the JSON line reports the count that ran.
+
 `--workload D1` / `D2` time the split-KV path (mifa_attention_splitkv) on few queries against a
 long key/value cache; the metric is HBM throughput of the compulsory bytes (Q, K, V read once,
 O and LSE written once).
@@ -42,6 +45,33 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+MIN_WARMUP_STEPS = 30
+WARMUP_SECONDS = 0.5
+
+
+def warm_up(step, requested) -> int:
+    """Untimed warm-up launches; returns how many ran.  With --warmup W exactly W; by default at
+    least MIN_WARMUP_STEPS launches and at least WARMUP_SECONDS of wall time, so that the GPU
+    clock has left its idle state before the timed region (short workloads otherwise finish
+    their warm-up within milliseconds)."""
+    import torch
+
+    if requested is not None:
+        for _ in range(requested):
+            step()
+        torch.cuda.synchronize()
+        return requested
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(10):
+            step()
+        n += 10
+        torch.cuda.synchronize()
+        if n >= MIN_WARMUP_STEPS and time.perf_counter() - t0 >= WARMUP_SECONDS:
+            return n
 
 
 def flops(w) -> float:
@@ -226,9 +256,7 @@ def bench_decode(args):
         if st != 0:
             raise binding.MifaError(st, binding.mifa_status_string(st))
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    args.warmup = warm_up(step, args.warmup)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -319,9 +347,7 @@ def bench_softmax(args):
     def step():
         binding.mifa_softmax_rows(dx, y, lse, w.rows, w.cols, dtype, w.scale, stream.cuda_stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    args.warmup = warm_up(step, args.warmup)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -413,9 +439,7 @@ def bench_backward(args):
         if st != 0:
             raise binding.MifaError(st, binding.mifa_status_string(st))
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    args.warmup = warm_up(step, args.warmup)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -499,7 +523,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up launches (default: at least 30 and at least 0.5 s of them)")
     ap.add_argument("--workload", default="C4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=131072)
@@ -540,9 +565,7 @@ def main():
     def step():
         binding.mifa_fwd(dq, dk, dv, o, lse, w.B, w.H, w.N, w.d, w.causal, scale, stream.cuda_stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    args.warmup = warm_up(step, args.warmup)
     log(f"warmup {args.warmup} done")
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]

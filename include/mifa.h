@@ -20,8 +20,10 @@
  * Conventions for every entry point:
  *   - Pointers named q, k, v, o, lse, x, y are DEVICE pointers (hipMalloc'd or equivalent) on
  *     the current HIP device.  The caller allocates and owns them; the library allocates
- *     nothing, keeps no pointer after returning and has no mutable global state, so calls
- *     are thread-safe and re-entrant.
+ *     nothing and keeps no pointer after returning.  Its only state across calls is the
+ *     per-thread code read by mifa_last_hip_error and, per kernel, an atomic record of the
+ *     devices on which that kernel's dynamic-LDS limit has already been raised (set on its
+ *     first launch there); calls are thread-safe and re-entrant.
  *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.  Work is
  *     enqueued asynchronously on it and the library never synchronises.  The caller must
  *     keep every buffer alive and unmodified until the stream has passed the kernel.

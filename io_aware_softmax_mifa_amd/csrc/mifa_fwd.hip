@@ -704,13 +704,13 @@ hipError_t launch(const Problem& pr, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Launch-shape choice: 8-wave workgroups (256 rows, one per CU) for long sequences with at least
-// as many of them as CUs; otherwise 4-wave workgroups (128 rows, two per CU).  Measured on
-// MI355X: B=1 H=32 N=16384 causal runs ~5 % faster with 8 waves, B=8 H=16 N=2048 causal ~9 %
-// faster with 4 (shorter tiles, better balance); N=4096 is about even.  Key-range splits always
-// use 4-wave workgroups.
+// Launch-shape choice: 8-wave workgroups (256 rows, one per CU) for sequences longer than 1024
+// with at least as many of them as CUs; otherwise 4-wave workgroups (128 rows, two per CU).
+// Measured on MI355X (same-box A/B): with 8 waves B=1 H=32 N=16384 causal runs ~8 % faster,
+// B=2 H=16 N=4096 causal ~7 % and B=8 H=16 N=2048 causal ~3 %.  Key-range splits always use
+// 4-wave workgroups.
 constexpr int kCUs = 256;
-constexpr int kLongN = 4096;
+constexpr int kLongN = 1024;
 template <int D, bool CAUSAL>
 hipError_t dispatch(const Problem& pr, hipStream_t stream) {
   const int64_t big_tiles = (int64_t)pr.BH * ((pr.Nq + 255) / 256);

@@ -37,6 +37,8 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E, published
+RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # 312.5
+LLC_BYTES = 256 << 20      # MI355X last-level (Infinity) cache
 KERNEL_SOURCE = os.path.join(ROOT, "io_aware_softmax_mifa_amd", "csrc", "mifa_fwd.hip")
 BWD_SOURCE = os.path.join(ROOT, "io_aware_softmax_mifa_amd", "csrc", "mifa_bwd.hip")
 SOFTMAX_SOURCE = os.path.join(ROOT, "io_aware_softmax_mifa_amd", "csrc", "mifa_softmax.hip")
@@ -529,6 +531,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=131072)
     ap.add_argument("--cpu-rows-softmax", type=int, default=0, help="0: every row")
+    ap.add_argument("--cold", action="store_true",
+                    help="forward legs: rotate through input/output copies larger than twice the LLC")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain device copy of known size (for HBM counter calibration)")
     args = ap.parse_args()
@@ -557,16 +561,25 @@ def main():
     q, k, v = W.make_workload_inputs(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    dq, dk, dv = (t.to(dev) for t in (q, k, v))
-    o = torch.empty(w.shape, dtype=torch.float32, device=dev)
-    lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+    cb = compulsory_bytes(w)
+    # --cold: rotate through enough copies of the inputs and outputs that the working set is
+    # more than twice the 256 MiB last-level cache, so every step's bytes come from HBM.
+    copies = (2 * LLC_BYTES) // cb + 2 if args.cold else 1
+    bufs = []
+    for _ in range(copies):
+        bufs.append((*(t.to(dev) for t in (q, k, v)), torch.empty(w.shape, dtype=torch.float32, device=dev),
+                     torch.empty(w.shape[:3], dtype=torch.float32, device=dev)))
+    o, lse = bufs[0][3], bufs[0][4]
     stream = torch.cuda.current_stream(dev)
+    turn = [0]
 
     def step():
-        binding.mifa_fwd(dq, dk, dv, o, lse, w.B, w.H, w.N, w.d, w.causal, scale, stream.cuda_stream)
+        dq, dk, dv, oo, ll = bufs[turn[0] % copies]
+        turn[0] += 1
+        binding.mifa_fwd(dq, dk, dv, oo, ll, w.B, w.H, w.N, w.d, w.causal, scale, stream.cuda_stream)
 
     args.warmup = warm_up(step, args.warmup)
-    log(f"warmup {args.warmup} done")
+    log(f"warmup {args.warmup} done" + (f" ({copies} rotating copies, {copies * cb / 2**20:.0f} MiB)" if args.cold else ""))
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -585,7 +598,7 @@ def main():
     f = flops(w)
     value = f / (ms_per_step * 1e-3) / 1e12
     achieved = f / (kernel_ms * 1e-3) / 1e12
-    cb = compulsory_bytes(w)
+    gbs = cb / (kernel_ms * 1e-3) / 1e9
 
     if args.copy_calibration:
         copy_calibration(dev)
@@ -611,16 +624,20 @@ def main():
             "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS,
             "kernel_ms": kernel_ms,
             "compulsory_hbm_bytes": cb,
+            "compulsory_gbs": gbs,
+            "flop_per_byte": f / cb,
+            "cold_cache": bool(args.cold),
+            "rotating_copies": copies,
         },
-        "roofline": {
-            "bound": "mfma",
-            "achieved": achieved,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": measured_traffic(w.name),
-        },
+        # The bound is the one the arithmetic intensity implies: below the ridge (peak FLOP/s over
+        # peak HBM bytes/s, 312.5 FLOP/B) the compulsory bytes, above it the FLOPs.
+        "roofline": (
+            {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": achieved / PEAK_BF16_TFLOPS}
+            if f / cb >= RIDGE_FLOP_PER_BYTE else
+            {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}),
     }
+    out["roofline"]["traffic"] = measured_traffic(w.name + ("-cold" if args.cold else ""))
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_rows} sampled rows")
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, scale, args.cpu_rows)

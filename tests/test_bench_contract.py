@@ -41,3 +41,18 @@ def test_json_line(workload):
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+
+
+@pytest.mark.gpu
+def test_cold_cache_leg():
+    """--cold rotates through copies whose total exceeds twice the 256 MiB last-level cache, and a
+    workload below the ridge (C2 causal, 204 FLOP/B) reports the HBM roofline in GB/s."""
+    r = run_bench("--workload", "C2-c", "--cold", "--steps", "3", "--warmup", "1", "--no-cpu-baseline")
+    print(r.stderr[-2000:], flush=True)
+    assert r.returncode == 0
+    d = json.loads([l for l in r.stdout.splitlines() if l.strip()][0])
+    c = d["config"]
+    assert c["cold_cache"] is True and c["rotating_copies"] * c["compulsory_hbm_bytes"] > 2 * (256 << 20)
+    rf = d["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert abs(rf["achieved"] - c["compulsory_gbs"]) < 1e-6 * rf["achieved"]

@@ -112,3 +112,23 @@ def test_splitkv_rejects_small_workspace():
 def test_decode_workloads(name):
     w = W.decode_by_name(name)
     case(w.B, w.H, w.Nq, w.Nk, w.d, w.causal, w.seed, split=True, dist=w.dist)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_rectangular_long_launch_shape(d, causal):
+    """Nq > 1024 with at least 256 query tiles of 256 rows takes the 8-wave launch; with Nq < Nk
+    the causal diagonal is shifted by Nk - Nq, which decides where each wave stops.  Nq = 1100 also
+    ends in a partial query tile and Nk = 1500 in a partial key block.  Three heads against the
+    oracle."""
+    from io_aware_softmax_mifa_amd import binding
+
+    B, H, Nq, Nk = 1, 64, 1100, 1500
+    q, k, v = W.make_rect_inputs(B, H, Nq, Nk, d, 31 + d, "normal")
+    scale = W.fp32_scale(d)
+    say(f"long rect: B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal}")
+    o, lse = run(binding.attention, q, k, v, causal, scale)
+    for h in (0, 37, H - 1):
+        ro, rl = attention_fp64(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], causal=causal, scale=scale)
+        check(o[:, h:h + 1], lse[:, h:h + 1], ro, rl, f"long rect d={d} causal={causal} head {h}")
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()

@@ -165,3 +165,20 @@ def test_custom_op_lower_right_and_mqa():
     # the shared head's gradient is the sum over the query heads
     check_grads((tq.grad, tk.grad, tv.grad), (rdq, rdk.sum(axis=1, keepdims=True), rdv.sum(axis=1, keepdims=True)),
                 "sdpa one kv head", True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_strided_bf16_long_launch_shape(d):
+    """[B, N, H, d] storage with bf16 O on the 8-wave launch (Nq > 1024, at least 256 query tiles
+    of 256 rows), rectangular and causal.  Three heads against the oracle."""
+    from io_aware_softmax_mifa_amd import binding
+
+    B, H, Nq, Nk = 1, 64, 1100, 1300
+    (q, k, v), (gq, gk, gv) = bnhd_views(B, H, Nq, Nk, d, 420 + d)
+    scale = W.fp32_scale(d)
+    out = torch.empty((B, Nq, H, d), dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    o, lse = binding.attention(gq, gk, gv, causal=True, scale=scale, out=out)
+    torch.cuda.synchronize()
+    for h in (0, 21, H - 1):
+        ro, rl = attention_fp64(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], causal=True, scale=scale)
+        check_o(o[:, h:h + 1], lse[:, h:h + 1], ro, rl, f"strided bf16 long d={d} head {h}", True)

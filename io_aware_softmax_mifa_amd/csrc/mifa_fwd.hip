@@ -705,16 +705,17 @@ hipError_t launch(const Problem& pr, hipStream_t stream) {
 }
 
 // Launch-shape choice: 8-wave workgroups (256 rows, one per CU) for sequences longer than 1024
-// with at least as many of them as CUs; otherwise 4-wave workgroups (128 rows, two per CU).
-// Measured on MI355X (same-box A/B): with 8 waves B=1 H=32 N=16384 causal runs ~8 % faster,
-// B=2 H=16 N=4096 causal ~7 % and B=8 H=16 N=2048 causal ~3 %.  Key-range splits always use
-// 4-wave workgroups.
+// with more of them than CUs; otherwise 4-wave workgroups (128 rows, two per CU).  Measured on
+// MI355X (same-box A/B): with 8 waves B=1 H=32 N=16384 causal runs ~8 % faster, B=2 H=16
+// N=4096 causal ~7 % and B=8 H=16 N=2048 causal ~3 %; with exactly one 256-row tile per CU
+// (B=1 H=4 N=16384, B=1 H=8 N=8192) 4 waves are 1-2.5 % faster, since two workgroups per CU
+// even out the causal triangle a little.  Key-range splits always use 4-wave workgroups.
 constexpr int kCUs = 256;
 constexpr int kLongN = 1024;
 template <int D, bool CAUSAL>
 hipError_t dispatch(const Problem& pr, hipStream_t stream) {
   const int64_t big_tiles = (int64_t)pr.BH * ((pr.Nq + 255) / 256);
-  if (pr.n_splits == 1 && pr.Nq > kLongN && big_tiles >= kCUs) return launch<Cfg<D, 64, 8, 4>, CAUSAL>(pr, stream);
+  if (pr.n_splits == 1 && pr.Nq > kLongN && big_tiles > kCUs) return launch<Cfg<D, 64, 8, 4>, CAUSAL>(pr, stream);
   return launch<Cfg<D, 64, 4, 2>, CAUSAL>(pr, stream);
 }
 

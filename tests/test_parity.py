@@ -93,7 +93,7 @@ def test_large_configs_sampled(name):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dist", ["normal", "stress"])
 def test_long_sequence_launch_shape(d, causal, dist):
-    """N > 1024 with at least 256 workgroups of 256 rows takes the 8-wave launch; N = 4133 also
+    """N > 1024 with more than 256 workgroups of 256 rows takes the 8-wave launch; N = 4133 also
     ends in a partial key block.  Two whole heads and 128 sampled rows against the oracle."""
     B, H, N = 1, 16, 4133
     q, k, v = W.make_inputs(B, H, N, d, seed=4133 + d, dist=dist)

@@ -117,7 +117,7 @@ def test_decode_workloads(name):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_rectangular_long_launch_shape(d, causal):
-    """Nq > 1024 with at least 256 query tiles of 256 rows takes the 8-wave launch; with Nq < Nk
+    """Nq > 1024 with more than 256 query tiles of 256 rows takes the 8-wave launch; with Nq < Nk
     the causal diagonal is shifted by Nk - Nq, which decides where each wave stops.  Nq = 1100 also
     ends in a partial query tile and Nk = 1500 in a partial key block.  Three heads against the
     oracle."""

@@ -169,7 +169,7 @@ def test_custom_op_lower_right_and_mqa():
 
 @pytest.mark.parametrize("d", [64, 128])
 def test_strided_bf16_long_launch_shape(d):
-    """[B, N, H, d] storage with bf16 O on the 8-wave launch (Nq > 1024, at least 256 query tiles
+    """[B, N, H, d] storage with bf16 O on the 8-wave launch (Nq > 1024, more than 256 query tiles
     of 256 rows), rectangular and causal.  Three heads against the oracle."""
     from io_aware_softmax_mifa_amd import binding
 

@@ -76,6 +76,18 @@ def warm_up(step, requested) -> int:
             return n
 
 
+def forward_roofline(f: float, cb: int, kernel_ms: float) -> dict:
+    """Roofline entry of a forward leg: the bound the arithmetic intensity implies.  Below the
+    ridge (peak FLOP/s over peak HBM bytes/s, 312.5 FLOP/B) the compulsory bytes per second
+    against 8 TB/s; at or above it the FLOPs per second against 2.5 PFLOP/s."""
+    if f / cb >= RIDGE_FLOP_PER_BYTE:
+        achieved = f / (kernel_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS}
+    gbs = cb / (kernel_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}
+
+
 def flops(w) -> float:
     f = 4.0 * w.B * w.H * w.N * w.N * w.d
     return f / 2 if w.causal else f
@@ -597,7 +609,6 @@ def main():
 
     f = flops(w)
     value = f / (ms_per_step * 1e-3) / 1e12
-    achieved = f / (kernel_ms * 1e-3) / 1e12
     gbs = cb / (kernel_ms * 1e-3) / 1e9
 
     if args.copy_calibration:
@@ -629,13 +640,7 @@ def main():
             "cold_cache": bool(args.cold),
             "rotating_copies": copies,
         },
-        # The bound is the one the arithmetic intensity implies: below the ridge (peak FLOP/s over
-        # peak HBM bytes/s, 312.5 FLOP/B) the compulsory bytes, above it the FLOPs.
-        "roofline": (
-            {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-             "frac": achieved / PEAK_BF16_TFLOPS}
-            if f / cb >= RIDGE_FLOP_PER_BYTE else
-            {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}),
+        "roofline": forward_roofline(f, cb, kernel_ms),
     }
     out["roofline"]["traffic"] = measured_traffic(w.name + ("-cold" if args.cold else ""))
     if not args.no_cpu_baseline:

@@ -56,3 +56,28 @@ def test_cold_cache_leg():
     rf = d["roofline"]
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert abs(rf["achieved"] - c["compulsory_gbs"]) < 1e-6 * rf["achieved"]
+
+
+def test_forward_roofline_choice_and_formulas():
+    """Host logic of the forward legs: FLOPs 4 B H N^2 d (halved when causal), compulsory bytes
+    (bf16 Q, K, V read once, fp32 O and LSE written once), and the roofline the arithmetic
+    intensity implies (ridge 2.5e15 / 8e12 = 312.5 FLOP/B)."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from io_aware_softmax_mifa_amd import workloads as W
+
+    assert bench.RIDGE_FLOP_PER_BYTE == 312.5
+    w = W.by_name("C4")
+    assert bench.flops(w) == 4.0 * 32 * 16384 ** 2 * 128 / 2
+    assert bench.compulsory_bytes(w) == 673185792
+    expect = {"C1-nc": "hbm", "C1-c": "hbm", "C2-nc": "mfma", "C2-c": "hbm", "C3": "mfma", "C4": "mfma", "C5": "mfma"}
+    for name, bound in expect.items():
+        w = W.by_name(name)
+        f, cb = bench.flops(w), bench.compulsory_bytes(w)
+        r = bench.forward_roofline(f, cb, 1.0)
+        assert r["bound"] == bound, name
+        assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-12
+        if bound == "mfma":
+            assert r["unit"] == "TFLOP/s" and abs(r["achieved"] - f / 1e-3 / 1e12) < 1e-6 * r["achieved"]
+        else:
+            assert r["unit"] == "GB/s" and abs(r["achieved"] - cb / 1e-3 / 1e9) < 1e-6 * r["achieved"]

@@ -197,6 +197,32 @@ __device__ __forceinline__ void issue_dma(const __bf16* __restrict__ kbase, cons
   issue_dma<C>(kbase, vbase, smem, kblk, kbuf, vblk, vbuf, N, wave, lane, la, la.dk, la.dv);
 }
 
+// Wave `wave`'s share of the DMA of key block blk of K (IS_V false) or V into that tensor's
+// LDS buffer buf; od: that share's per-lane source offsets within a full block.  Rows past the
+// end of the sequence are clamped to the last row, as in issue_dma.
+template <typename C, bool IS_V>
+__device__ __forceinline__ void issue_one(const __bf16* __restrict__ base, char* smem, int blk, int buf, int N,
+                                          int wave, int lane, const Lane<C>& la,
+                                          const unsigned (&od)[C::kInstPerWave]) {
+  constexpr int BC = C::BC;
+  const char* src = (const char*)base + (int64_t)blk * BC * (IS_V ? la.vsb : la.ksb);
+  unsigned o[C::kInstPerWave];
+#pragma unroll
+  for (int t = 0; t < C::kInstPerWave; ++t) o[t] = od[t];
+  if (blk * BC + BC > N) {
+    unsigned ok[C::kInstPerWave], ov[C::kInstPerWave];
+    dma_offsets<C>(ok, ov, wave, lane, N - 1 - blk * BC, la.ksb, la.vsb);
+#pragma unroll
+    for (int t = 0; t < C::kInstPerWave; ++t) o[t] = IS_V ? ov[t] : ok[t];
+  }
+  char* dst = smem + (IS_V ? C::kVBase : 0) + buf * C::kTensorBytes;
+#pragma unroll
+  for (int t = 0; t < C::kInstPerWave; ++t) {
+    const int inst = wave * C::kInstPerWave + t;
+    __builtin_amdgcn_global_load_lds((global_cvoid*)(src + o[t]), (lds_void*)(dst + inst * 1024), 16, 0, 0);
+  }
+}
+
 // ---- the per-wave pipeline stages -------------------------------------------------------------
 template <typename C, bool CAUSAL>
 struct Wave {
@@ -559,24 +585,36 @@ void mifa_fwd_kernel(FwdParams p) {
     // waves meet at a barrier, and right after it the DMA of K(j+3), K(j+4), V(j+2), V(j+3)
     // goes out: the buffers blocks j-2 and j-1 have released.  Blocks j and j+1 read K(j+1),
     // K(j+2), V(j), V(j+1), all issued at the previous even barrier and waited for (vmcnt 0)
-    // before this one.  Between barriers the waves drift up to a block apart.
+    // before this one.  Loads past the last block are skipped.  Between barriers the waves drift
+    // up to a block apart.
     //   A load instruction holds up its wave for tens of cycles.  Inside the loop only the
     // high-priority waves issue, each its own share and that of the wave it shares a SIMD with:
     // they run ahead and would wait at the next barrier anyway, and while they issue, the other
     // wave of the SIMD keeps the matrix unit busy.
-    auto pair = [&](int kb, int vb) {
-      issue_dma<C>(kh, vh, smem, min(kb, last), kb % NBUF, min(vb, last), vb % NBUF, N, wave, lane, W.la);
+    auto ld = [&](int blk, int w, const unsigned (&odk)[C::kInstPerWave], const unsigned (&odv)[C::kInstPerWave],
+                  bool is_v) {
+      if (blk > last) return;
+      if (is_v)
+        issue_one<C, true>(vh, smem, blk, blk % NBUF, N, w, lane, W.la, odv);
+      else
+        issue_one<C, false>(kh, smem, blk, blk % NBUF, N, w, lane, W.la, odk);
     };
-    auto pair2 = [&](int kb, int vb) {
-      issue_dma<C>(kh, vh, smem, min(kb, last), kb % NBUF, min(vb, last), vb % NBUF, N, wave, lane, W.la, W.la.dk,
-                   W.la.dv);
-      issue_dma<C>(kh, vh, smem, min(kb, last), kb % NBUF, min(vb, last), vb % NBUF, N, wave + C::WAVES / 2, lane,
-                   W.la, W.la.pdk, W.la.pdv);
+    auto both = [&](int blk, bool is_v) {
+      ld(blk, wave, W.la.dk, W.la.dv, is_v);
+      ld(blk, wave + C::WAVES / 2, W.la.pdk, W.la.pdv, is_v);
     };
-    pair(0, 0);
-    pair(1, 1);
-    pair(2, 1);
-    wait_vmcnt<2 * C::kDmaPerGroup>();  // K(0) has landed
+    // Prologue, every wave its own share: K(0), V(0), K(1), V(1), K(2).
+    ld(0, wave, W.la.dk, W.la.dv, false);
+    ld(0, wave, W.la.dk, W.la.dv, true);
+    ld(1, wave, W.la.dk, W.la.dv, false);
+    ld(1, wave, W.la.dk, W.la.dv, true);
+    ld(2, wave, W.la.dk, W.la.dv, false);
+    if (last >= 2)  // K(0) has landed (the loads issued after it may still be in flight)
+      wait_vmcnt<4 * C::kInstPerWave>();
+    else if (last == 1)
+      wait_vmcnt<3 * C::kInstPerWave>();
+    else
+      wait_vmcnt<C::kInstPerWave>();
     __builtin_amdgcn_s_barrier();
     W.first_scores(sA);
     auto step = [&]<int U>(int j, f32x16(&cur)[C::kKT], f32x16(&nxt)[C::kKT], IC<U>) {
@@ -584,15 +622,17 @@ void mifa_fwd_kernel(FwdParams p) {
         wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();
         if (wave < C::WAVES / 2) {
-          pair2(j + 3, j + 2);
-          pair2(j + 4, j + 3);
+          both(j + 3, false);
+          both(j + 2, true);
+          both(j + 4, false);
+          both(j + 3, true);
         }
       }
       if (j < nblk_w) W.template block<(U + 1) % NBUF, U % NBUF>(cur, nxt, j * BC, j >= j_mask);
     };
     for (int j0 = 0; j0 < nblk; j0 += C::kUnroll) {
       [&]<int... U>(std::integer_sequence<int, U...>) {
-        ((j0 + U < nblk ? (U % 2 == 0 ? step(j0 + U, sA, sB, IC<U>{}) : step(j0 + U, sB, sA, IC<U>{})), true : false) && ...);
+        (void)((j0 + U < nblk ? (U % 2 == 0 ? step(j0 + U, sA, sB, IC<U>{}) : step(j0 + U, sB, sA, IC<U>{})), true : false) && ...);
       }(std::make_integer_sequence<int, C::kUnroll>{});
     }
   } else {
@@ -625,7 +665,7 @@ void mifa_fwd_kernel(FwdParams p) {
   };
   for (int j0 = 0; j0 < nblk; j0 += C::kUnroll) {
     [&]<int... U>(std::integer_sequence<int, U...>) {
-      ((j0 + U < nblk ? (U % 2 == 0 ? step(j0 + U, sA, sB, IC<U>{}) : step(j0 + U, sB, sA, IC<U>{})), true : false) && ...);
+      (void)((j0 + U < nblk ? (U % 2 == 0 ? step(j0 + U, sA, sB, IC<U>{}) : step(j0 + U, sB, sA, IC<U>{})), true : false) && ...);
     }(std::make_integer_sequence<int, C::kUnroll>{});
   }
   }

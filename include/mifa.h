@@ -52,7 +52,8 @@ typedef enum mifa_status {
   MIFA_ERR_BAD_DTYPE = 8,      /* dtype is not one of mifa_dtype (mifa_softmax_rows) */
   MIFA_ERR_WORKSPACE = 9,      /* workspace NULL, misaligned or too small (mifa_attention_splitkv,
                                   mifa_bwd) */
-  MIFA_ERR_BAD_STRIDE = 10     /* a stride is negative (the *_strided entry points) */
+  MIFA_ERR_BAD_STRIDE = 10,    /* a stride is negative (the *_strided entry points) */
+  MIFA_ERR_SCRATCH = 11        /* mifa_attention_splitkv_noalloc: partials exceed its 32 MiB array */
 } mifa_status;
 
 /* Element types of mifa_softmax_rows. */
@@ -147,6 +148,25 @@ int mifa_attention_splitkv(const void* q, const void* k, const void* v, float* o
 
 /* Workspace bytes mifa_attention_splitkv needs for this shape (0 for an invalid shape). */
 int64_t mifa_splitkv_workspace_bytes(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d);
+
+/*
+ * mifa_attention_splitkv_noalloc -- mifa_attention_splitkv for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops or harnesses that forbid hipMalloc):
+ * the key-range partials live in a static 32 MiB device array of the library instead of a
+ * caller workspace.  Same arguments (no workspace), same kernels and the same result, bit for bit.
+ *   - The call itself calls no hipMalloc, hipFree or other allocating routine.  Each device holds
+ *     its own copy of the array from the library's loading until the process ends; its address is
+ *     resolved on the first call on that device.
+ *   - The array is shared by every call on one device and keeps the last call's contents; calls
+ *     that may overlap on one device race and must be ordered on one stream.  Nothing in it needs
+ *     clearing: every call writes all the partials it reads.
+ *   - MIFA_ERR_SCRATCH, checked after the other arguments and before any HIP call, when the
+ *     partials (mifa_splitkv_workspace_bytes of the shape) exceed 32 MiB.  Errors otherwise as for
+ *     mifa_attention_splitkv without MIFA_ERR_WORKSPACE.
+ */
+int mifa_attention_splitkv_noalloc(const void* q, const void* k, const void* v, float* o, float* lse,
+                                   int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal,
+                                   float scale, void* stream);
 
 /*
  * mifa_bwd -- gradients of mifa_attention with respect to q, k and v.

@@ -28,9 +28,11 @@ STATUS_NAMES = {
     8: "MIFA_ERR_BAD_DTYPE",
     9: "MIFA_ERR_WORKSPACE",
     10: "MIFA_ERR_BAD_STRIDE",
+    11: "MIFA_ERR_SCRATCH",
 }
 MIFA_DTYPE_BF16, MIFA_DTYPE_F32 = 0, 1
 EXPORTED = ("mifa_fwd", "mifa_attention", "mifa_attention_strided", "mifa_attention_splitkv",
+            "mifa_attention_splitkv_noalloc",
             "mifa_splitkv_workspace_bytes", "mifa_bwd", "mifa_bwd_strided", "mifa_bwd_workspace_bytes",
             "mifa_softmax_rows", "mifa_status_string", "mifa_version", "mifa_last_hip_error")
 
@@ -57,6 +59,9 @@ def _load() -> ctypes.CDLL:
                                            [ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int64,
                                             ctypes.c_void_p])
     lib.mifa_attention_splitkv.restype = ctypes.c_int
+    lib.mifa_attention_splitkv_noalloc.argtypes = ([ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 +
+                                                   [ctypes.c_int, ctypes.c_float, ctypes.c_void_p])
+    lib.mifa_attention_splitkv_noalloc.restype = ctypes.c_int
     lib.mifa_splitkv_workspace_bytes.argtypes = [ctypes.c_int64] * 5
     lib.mifa_splitkv_workspace_bytes.restype = ctypes.c_int64
     lib.mifa_bwd.argtypes = ([ctypes.c_void_p] * 9 + [ctypes.c_int64] * 5 +
@@ -143,6 +148,13 @@ def mifa_attention_splitkv_raw(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, 
     return int(_lib.mifa_attention_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H), int(Nq),
                                            int(Nk), int(d), 1 if causal else 0, float(scale), _ptr(workspace),
                                            int(workspace_bytes), stream or None))
+
+
+def mifa_attention_splitkv_noalloc_raw(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale, stream) -> int:
+    """The allocation-free split-KV entry point (partials in the library's static device array)."""
+    return int(_lib.mifa_attention_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
+                                                   int(Nq), int(Nk), int(d), 1 if causal else 0, float(scale),
+                                                   stream or None))
 
 
 def mifa_splitkv_workspace_bytes(B, H, Nq, Nk, d) -> int:

@@ -860,6 +860,70 @@ int check_strides(const int64_t* st, int n) {
 
 thread_local int g_last_hip_error = 0;
 
+// The split-KV launches after validation: the split kernel writes each key range's partial O and
+// LSE to `workspace` (unused when one range suffices), then merge_splits combines them.
+int splitkv_run(const void* q, const void* k, const void* v, float* o, float* lse, int64_t H, int64_t BH, int64_t Nq,
+                int64_t Nk, int64_t d, int causal, float scale, const Split& sp, void* workspace, hipStream_t s) {
+  hipError_t e;
+  if (sp.n_splits == 1) {
+    Problem pr{q, k, v, o, lse, (int)Nq, (int)Nk, (int)BH, scale, 1, sp.split_blocks, 0, 0, (int)H, 0, {}};
+    dense_strides(H, Nq, Nk, d, pr.st);
+    e = dispatch_d(pr, (int)d, causal != 0, s);
+  } else {
+    float* o_part = (float*)workspace;
+    float* lse_part = o_part + (int64_t)sp.n_splits * BH * Nq * d;
+    Problem pr{q,          k,  v,  o_part, lse_part, (int)Nq, (int)Nk, (int)BH, scale, sp.n_splits, sp.split_blocks,
+               BH * Nq * d, BH * Nq, (int)H, 0, {}};
+    dense_strides(H, Nq, Nk, d, pr.st);
+    e = dispatch_d(pr, (int)d, causal != 0, s);
+    if (e == hipSuccess) {
+      const int64_t rows = BH * Nq;
+      const int rpb = kMergeThreads / ((int)d / 4);
+      const unsigned blocks = (unsigned)((rows + rpb - 1) / rpb);
+      if (d == 128)
+        hipLaunchKernelGGL(merge_splits<128>, dim3(blocks), dim3(kMergeThreads), 0, s, o_part, lse_part, o, lse, rows,
+                           sp.n_splits, BH * Nq * d, BH * Nq);
+      else
+        hipLaunchKernelGGL(merge_splits<64>, dim3(blocks), dim3(kMergeThreads), 0, s, o_part, lse_part, o, lse, rows,
+                           sp.n_splits, BH * Nq * d, BH * Nq);
+      e = hipGetLastError();
+    }
+  }
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return MIFA_ERR_HIP;
+  }
+  return MIFA_OK;
+}
+
+// ---- allocation-free split-KV: the partials live in a static device array ----------------------
+// For callers that cannot allocate device memory (code under HIP graph capture, serving loops that
+// forbid hipMalloc).  Each device the library runs on holds its own copy of `scratch` until the
+// process ends.  In host code the array's name is only a stand-in for the symbol, not a device
+// address: the address is resolved with hipGetSymbolAddress once per device (with that device
+// current) and kept here; kernels receive that address.  Calls on one device share the array,
+// so calls that may overlap on one device must be ordered on a stream.  The split kernel writes
+// every row of every range before the merge reads it, so nothing needs clearing between calls.
+constexpr int64_t kScratchBytes = (int64_t)32 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);  // two threads may both resolve it: same value
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -920,37 +984,27 @@ int mifa_attention_splitkv(const void* q, const void* k, const void* v, float* o
   if (!workspace || ((uintptr_t)workspace & 15u) || workspace_bytes_given < workspace_bytes(BH, Nq, d, sp.n_splits))
     return MIFA_ERR_WORKSPACE;
   if (BH * ((Nq + 127) / 128) * sp.n_splits >= ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  if (sp.n_splits == 1) {
-    Problem pr{q, k, v, o, lse, (int)Nq, (int)Nk, (int)BH, scale, 1, sp.split_blocks, 0, 0, (int)H, 0, {}};
-    dense_strides(H, Nq, Nk, d, pr.st);
-    e = dispatch_d(pr, (int)d, causal != 0, s);
-  } else {
-    float* o_part = (float*)workspace;
-    float* lse_part = o_part + (int64_t)sp.n_splits * BH * Nq * d;
-    Problem pr{q,          k,  v,  o_part, lse_part, (int)Nq, (int)Nk, (int)BH, scale, sp.n_splits, sp.split_blocks,
-               BH * Nq * d, BH * Nq, (int)H, 0, {}};
-    dense_strides(H, Nq, Nk, d, pr.st);
-    e = dispatch_d(pr, (int)d, causal != 0, s);
-    if (e == hipSuccess) {
-      const int64_t rows = BH * Nq;
-      const int rpb = kMergeThreads / ((int)d / 4);
-      const unsigned blocks = (unsigned)((rows + rpb - 1) / rpb);
-      if (d == 128)
-        hipLaunchKernelGGL(merge_splits<128>, dim3(blocks), dim3(kMergeThreads), 0, s, o_part, lse_part, o, lse, rows,
-                           sp.n_splits, BH * Nq * d, BH * Nq);
-      else
-        hipLaunchKernelGGL(merge_splits<64>, dim3(blocks), dim3(kMergeThreads), 0, s, o_part, lse_part, o, lse, rows,
-                           sp.n_splits, BH * Nq * d, BH * Nq);
-      e = hipGetLastError();
+  return splitkv_run(q, k, v, o, lse, H, BH, Nq, Nk, d, causal, scale, sp, workspace, (hipStream_t)stream);
+}
+
+int mifa_attention_splitkv_noalloc(const void* q, const void* k, const void* v, float* o, float* lse, int64_t B,
+                                   int64_t H, int64_t Nq, int64_t Nk, int64_t d, int causal, float scale,
+                                   void* stream) {
+  const int st = check_attention(q, k, v, o, lse, B, H, Nq, Nk, d, causal, scale);
+  if (st != MIFA_OK) return st;
+  const int64_t BH = B * H;
+  const Split sp = choose_split(BH, Nq, Nk);
+  if (sp.n_splits > 1 && workspace_bytes(BH, Nq, d, sp.n_splits) > kScratchBytes) return MIFA_ERR_SCRATCH;
+  if (BH * ((Nq + 127) / 128) * sp.n_splits >= ((int64_t)1 << 31)) return MIFA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (sp.n_splits > 1) {
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) {
+      g_last_hip_error = (int)e;
+      return MIFA_ERR_HIP;
     }
   }
-  if (e != hipSuccess) {
-    g_last_hip_error = (int)e;
-    return MIFA_ERR_HIP;
-  }
-  return MIFA_OK;
+  return splitkv_run(q, k, v, o, lse, H, BH, Nq, Nk, d, causal, scale, sp, ws, (hipStream_t)stream);
 }
 
 const char* mifa_status_string(int status) {
@@ -966,6 +1020,8 @@ const char* mifa_status_string(int status) {
     case MIFA_ERR_BAD_DTYPE: return "dtype must be MIFA_DTYPE_BF16 or MIFA_DTYPE_F32";
     case MIFA_ERR_WORKSPACE: return "workspace NULL, not 16-byte aligned, or smaller than the entry point's *_workspace_bytes";
     case MIFA_ERR_BAD_STRIDE: return "a stride is negative";
+    case MIFA_ERR_SCRATCH:
+      return "the key-range partials need more than the 32 MiB static scratch array of the allocation-free entry point";
     default: return "unknown status";
   }
 }

@@ -21,7 +21,8 @@ def declared_functions():
 
 
 def test_header_declares_expected_api():
-    assert declared_functions() == ["mifa_attention", "mifa_attention_splitkv", "mifa_attention_strided", "mifa_bwd",
+    assert declared_functions() == ["mifa_attention", "mifa_attention_splitkv", "mifa_attention_splitkv_noalloc",
+                                    "mifa_attention_strided", "mifa_bwd",
                                     "mifa_bwd_strided", "mifa_bwd_workspace_bytes", "mifa_fwd",
                                     "mifa_last_hip_error", "mifa_softmax_rows", "mifa_splitkv_workspace_bytes",
                                     "mifa_status_string", "mifa_version"]
@@ -183,6 +184,16 @@ def test_splitkv_workspace_checks(lib):
     assert lib.mifa_attention_splitkv_raw(*args, A, need - 1, None) == 9      # too small
     # argument errors come first
     assert lib.mifa_attention_splitkv_raw(A, A, A, A, A, 1, 8, 2, 1, 128, 1, 0.1, 0, 0, None) == 2
+
+
+def test_splitkv_noalloc_checks(lib):
+    # argument errors first, then the 32 MiB limit of the static scratch array (no HIP call before)
+    assert lib.mifa_attention_splitkv_noalloc_raw(0, A, A, A, A, 1, 8, 1, 32768, 128, 1, 0.1, None) == 1
+    assert lib.mifa_attention_splitkv_noalloc_raw(A, A, A, A, A, 1, 8, 2, 1, 128, 1, 0.1, None) == 2
+    big = (1, 8, 512, 65536, 128)
+    assert lib.mifa_splitkv_workspace_bytes(*big) > 32 << 20
+    assert lib.mifa_attention_splitkv_noalloc_raw(A, A, A, A, A, *big, 1, 0.1, None) == 11
+    assert "32 MiB" in lib.mifa_status_string(11)
 
 
 def test_splitkv_workspace_bytes(lib):

@@ -20,6 +20,13 @@ O and LSE written once).
 `--workload SM1` .. `SM5` time the stand-alone row softmax (mifa_softmax_rows) instead: one
 step is one launch over a [rows, cols] matrix, and the metric is HBM throughput of the
 compulsory bytes (the input read once, the output and the row LSE written once).
+
+Besides the driver's fields, `roofline` and `cpu_baseline`, the line carries `provenance` (source
+hashes, git commit where available, GPU, ROCm/HIP/torch versions, seed); on the attention legs
+`clock`, the sustained engine clock sampled with amdsmi over a further second of untimed
+launches after the timed ones and the percentage of the peak at that clock; and on the forward
+legs `parity`, the errors of the last timed launch's O and LSE on the rows the CPU-baseline leg
+computed with the float64 oracle.
 """
 from __future__ import annotations
 
@@ -151,21 +158,168 @@ def host_info() -> dict:
     return {"host_cpus": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
 
 
+PEAK_CLOCK_MHZ = 2400.0    # MI355X peak engine clock, the clock the 2.5 PFLOP/s figure assumes
+CLOCK_WINDOW_S = 1.0       # untimed launches after the timed steps, during which the clock is sampled
+
+
+def sample_clock(step, value_tflops):
+    """The sustained engine clock under this workload: launches of the same step for about
+    CLOCK_WINDOW_S seconds after the timed region (untimed, not part of `value`), sampled with
+    amdsmi.  Returns the ClockSampler report with the clock-adjusted peak."""
+    import torch
+
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < CLOCK_WINDOW_S:
+            for _ in range(50):
+                step()
+            torch.cuda.synchronize()
+    return clock.result(value_tflops)
+SOURCES = [os.path.join(ROOT, "io_aware_softmax_mifa_amd", "csrc", f)
+           for f in ("mifa_fwd.hip", "mifa_bwd.hip", "mifa_softmax.hip", "mifa_common.h")]
+
+
+def provenance(seed) -> dict:
+    """What produced this line: source hashes, git commit (where the checkout has .git), GPU and
+    software versions, and the workload's seed."""
+    import subprocess
+
+    import torch
+
+    h = hashlib.sha256()
+    for path in SOURCES + [os.path.abspath(__file__)]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                             timeout=10).stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        sha = None
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        pass
+    props = torch.cuda.get_device_properties(0)
+    from io_aware_softmax_mifa_amd import binding
+
+    return {"git_sha": sha, "sources_sha256": h.hexdigest()[:16], "gpu_name": torch.cuda.get_device_name(0),
+            "gpu_arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
+            "rocm_version": rocm, "hip_runtime": torch.version.hip, "torch_version": torch.__version__,
+            "library": binding.mifa_version(), "seed": seed}
+
+
+class ClockSampler:
+    """Samples the GPU engine clock with amdsmi on a background thread (the launches are queued
+    asynchronously, so the thread does not delay the GPU).  The driver refreshes the clock it
+    reports only every few milliseconds, so the sampler is run over a window of about a second;
+    samples from the first `skip_s` seconds (the clock still settling) are dropped.  Reports the
+    mean over the kept samples, or None where amdsmi is unavailable."""
+
+    def __init__(self, period_s: float = 0.005, skip_s: float = 0.25):
+        self.period_s, self.skip_s, self.samples, self.error = period_s, skip_s, [], None
+
+    def _read(self):
+        import amdsmi
+
+        m = amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
+        if clks:
+            return sum(clks) / len(clks)
+        c = m.get("current_gfxclk")
+        if isinstance(c, (int, float)) and 0 < c < 10000:
+            return float(c)
+        return float(amdsmi.amdsmi_get_clock_info(self.handle, amdsmi.AmdSmiClkType.SYS)["clk"])
+
+    def _loop(self):
+        t0 = time.perf_counter()
+        while not self.stop:
+            try:
+                c = self._read()
+                if time.perf_counter() - t0 >= self.skip_s:
+                    self.samples.append(c)
+            except Exception as e:  # noqa: BLE001 -- a sampling failure only loses the clock figure
+                self.error = repr(e)
+                return
+            time.sleep(self.period_s)
+
+    def __enter__(self):
+        import threading
+
+        self.stop, self.thread = False, None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if len(handles) != 1:
+                raise RuntimeError(f"{len(handles)} GPUs visible to amdsmi; the clock would be ambiguous")
+            self.handle = handles[0]
+            self._read()
+            self.thread = threading.Thread(target=self._loop, daemon=True)
+            self.thread.start()
+        except Exception as e:  # noqa: BLE001
+            self.error = repr(e)
+        return self
+
+    def __exit__(self, *exc):
+        self.stop = True
+        if self.thread is not None:
+            self.thread.join()
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_shut_down()
+        except Exception:  # noqa: BLE001
+            pass
+        return False
+
+    def result(self, tflops: float | None = None) -> dict:
+        out = {"source": ("amdsmi gpu_metrics current_gfxclks (mean over XCDs per sample; the peak uses the median over samples), sampled every "
+                          f"{1e3 * self.period_s:g} ms over {CLOCK_WINDOW_S:g} s of further launches of the same "
+                          f"step after the timed steps, the first {self.skip_s:g} s dropped"),
+               "samples": len(self.samples), "mean_mhz": None, "min_mhz": None, "max_mhz": None,
+               "error": self.error}
+        if self.samples:
+            srt = sorted(self.samples)
+            out.update(mean_mhz=sum(srt) / len(srt), median_mhz=srt[len(srt) // 2], min_mhz=srt[0], max_mhz=srt[-1])
+            if tflops is not None:
+                # the median: samples that catch XCDs idle between launches would pull a mean down
+                peak = PEAK_BF16_TFLOPS * out["median_mhz"] / PEAK_CLOCK_MHZ
+                out["clock_adjusted_peak_tflops"] = peak
+                out["pct_of_clock_adjusted_peak"] = 100.0 * tflops / peak
+        return out
+
+
 def event_stats(starts, ends) -> dict:
     """Median and minimum per-call milliseconds from paired HIP events."""
     ms = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
     return {"call_ms_median": ms[len(ms) // 2], "call_ms_min": ms[0]}
 
 
-def cpu_baseline(w, q, k, v, scale, rows_count: int):
-    """The float64 oracle as it stands, timed on this host on a bounded sample of rows."""
+def cpu_baseline(w, q, k, v, scale, rows_count: int, o_gpu=None, lse_gpu=None):
+    """The float64 oracle as it stands, timed on this host on a bounded sample of rows.  With the
+    timed launch's outputs (o_gpu, lse_gpu on the host) the same oracle rows also give that
+    launch's parity: O max/mean-abs and LSE max-abs error on the sampled rows."""
+    import numpy as np
+
     from io_aware_softmax_mifa_amd import workloads as W
     from oracle import attention_fp64_rows
 
     rows = W.sample_rows(w.B, w.H, w.N, rows_count, w.seed + 7)
     t0 = time.perf_counter()
-    attention_fp64_rows(q, k, v, rows, causal=w.causal, scale=scale)
+    ro, rl = attention_fp64_rows(q, k, v, rows, causal=w.causal, scale=scale)
     dt = time.perf_counter() - t0
+    parity = None
+    if o_gpu is not None:
+        r = rows.numpy()
+        err = np.abs(o_gpu[r[:, 0], r[:, 1], r[:, 2]].double().numpy() - ro)
+        lerr = np.abs(lse_gpu[r[:, 0], r[:, 1], r[:, 2]].double().numpy() - rl)
+        parity = {"rows": int(r.shape[0]), "o_max_abs": float(err.max()), "o_mean_abs": float(err.mean()),
+                  "lse_max_abs": float(lerr.max()), "bar": {"o_max_abs": 2e-2, "o_mean_abs": 2e-3, "lse_max_abs": 1e-3}}
+        parity["pass"] = bool(parity["o_max_abs"] <= 2e-2 and parity["o_mean_abs"] <= 2e-3
+                              and parity["lse_max_abs"] <= 1e-3)
     # Credit each sampled row with the per-row share of the step's FLOP convention.
     per_row = flops(w) / (w.B * w.H * w.N)
     value = rows.shape[0] * per_row / dt / 1e12
@@ -182,7 +336,7 @@ def cpu_baseline(w, q, k, v, scale, rows_count: int):
         "extrapolated_full_oracle_seconds": dt * (w.B * w.H * w.N) / rows.shape[0],
     }
     out.update(host_info())
-    return out
+    return out, parity
 
 
 def copy_calibration(dev):
@@ -319,6 +473,7 @@ def bench_decode(args):
             "traffic": measured_traffic(w.name, KERNEL_SOURCE),
         },
     }
+    out["provenance"] = provenance(w.seed)
     if args.no_cpu_baseline:
         out["cpu_baseline"] = None
     else:
@@ -408,6 +563,7 @@ def bench_softmax(args):
             "traffic": measured_traffic(w.name, SOFTMAX_SOURCE),
         },
     }
+    out["provenance"] = provenance(w.seed)
     out["cpu_baseline"] = None if args.no_cpu_baseline else softmax_cpu_baseline(w, x, args.cpu_rows_softmax)
     out["config"].update(event_stats(starts, ends))
     print(json.dumps(out), flush=True)
@@ -506,6 +662,8 @@ def bench_backward(args):
             "kernels": "row_dot + dq + dkdv (one mifa_bwd call)",
         },
     }
+    out["clock"] = sample_clock(step, value)
+    out["provenance"] = provenance(w.seed)
     if args.no_cpu_baseline:
         out["cpu_baseline"] = None
     else:
@@ -606,6 +764,8 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kernel_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step wall, {kernel_ms:.4f} ms/launch (HIP events)")
+    # outputs of the last timed launch, for its parity against the oracle rows of the CPU baseline
+    last_o, last_lse = bufs[(turn[0] - 1) % copies][3].cpu(), bufs[(turn[0] - 1) % copies][4].cpu()
 
     f = flops(w)
     value = f / (ms_per_step * 1e-3) / 1e12
@@ -615,7 +775,8 @@ def main():
         copy_calibration(dev)
 
     out = {
-        "metric": "attention fwd TFLOP/s (bf16, causal) and % of MI355X bf16 MFMA peak",
+        "metric": (f"attention fwd TFLOP/s (bf16, {'causal' if w.causal else 'non-causal'}) and % of MI355X bf16 "
+                   "MFMA peak"),
         "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -643,11 +804,18 @@ def main():
         "roofline": forward_roofline(f, cb, kernel_ms),
     }
     out["roofline"]["traffic"] = measured_traffic(w.name + ("-cold" if args.cold else ""))
+    out["clock"] = sample_clock(step, value)
+    if out["clock"].get("pct_of_clock_adjusted_peak") is not None:
+        log(f"sustained clock {out['clock']['median_mhz']:.0f} MHz: {out['clock']['pct_of_clock_adjusted_peak']:.1f}% of "
+            "the peak at that clock")
+    out["provenance"] = provenance(w.seed)
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_rows} sampled rows")
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, scale, args.cpu_rows)
+        out["cpu_baseline"], out["parity"] = cpu_baseline(w, q, k, v, scale, args.cpu_rows, last_o, last_lse)
+        log(f"parity of the last timed launch on {out['parity']['rows']} rows: O max {out['parity']['o_max_abs']:.3e} "
+            f"mean {out['parity']['o_mean_abs']:.3e}, LSE max {out['parity']['lse_max_abs']:.3e}")
     else:
-        out["cpu_baseline"] = None
+        out["cpu_baseline"], out["parity"] = None, None
     out["config"].update(event_stats(starts, ends))
     print(json.dumps(out), flush=True)
 

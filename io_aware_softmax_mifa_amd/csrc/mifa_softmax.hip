@@ -123,7 +123,8 @@ constexpr bool kPackedRow = sizeof(T) == 2 && EPT >= 64;
 
 // NT threads per workgroup (NT/64 waves), WPR waves per row, EPT elements per thread.
 template <typename T, int WPR, int EPT, int NT>
-__global__ __launch_bounds__(NT) void softmax_resident(const T* __restrict__ x, T* __restrict__ y,
+// y may be x (in place): every store of a row follows the reduction over all of its loaded values.
+__global__ __launch_bounds__(NT) void softmax_resident(const T* x, T* y,
                                                        float* __restrict__ lse, int64_t rows, int cols, float c,
                                                        int vec_ok) {
   using E = Elem<T>;
@@ -316,7 +317,7 @@ __device__ __forceinline__ void store_part(T* yr, int cols, int base, int u, int
 
 // ---- streaming rows (longer than a workgroup's registers hold) ------------------------------
 template <typename T>
-__global__ __launch_bounds__(kThreads) void softmax_stream(const T* __restrict__ x, T* __restrict__ y,
+__global__ __launch_bounds__(kThreads) void softmax_stream(const T* x, T* y,
                                                             float* __restrict__ lse, int cols, float c, int vec_ok) {
   using E = Elem<T>;
   constexpr int V = E::kVec, U = 4;  // U vectors in flight per thread per step
@@ -360,16 +361,16 @@ __global__ __launch_bounds__(kThreads) void softmax_stream(const T* __restrict__
   for (int w = 1; w < 4; ++w) merge(m, l, red[0][w], red[1][w]);
   const float inv = 1.f / l;
 
-  // pass 2: normalise
+  // pass 2: normalise.  y may be x (in place): every element is read and written by the same
+  // thread, and a step's U loads are all issued before its stores, so no store overtakes a load.
   for (int base = 0; base < cols; base += kStep) {
+    float v[U * V];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float v[V];
-      load_part<T>(xr, cols, base, u, tid, vec_ok, v);
+    for (int u = 0; u < U; ++u) load_part<T>(xr, cols, base, u, tid, vec_ok, v + u * V);
 #pragma unroll
-      for (int i = 0; i < V; ++i) v[i] = __builtin_amdgcn_exp2f(scaled(v[i], c) - m) * inv;
-      store_part<T>(yr, cols, base, u, tid, vec_ok, v);
-    }
+    for (int i = 0; i < U * V; ++i) v[i] = __builtin_amdgcn_exp2f(scaled(v[i], c) - m) * inv;
+#pragma unroll
+    for (int u = 0; u < U; ++u) store_part<T>(yr, cols, base, u, tid, vec_ok, v + u * V);
   }
   if (lse && tid == 0) lse[row] = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
 }

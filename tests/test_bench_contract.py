@@ -41,6 +41,14 @@ def test_json_line(workload):
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    if workload == "C2-c":
+        # forward legs also carry provenance, the sampled clock and the timed launch's parity
+        pv = d["provenance"]
+        assert pv["seed"] == 102 and pv["gpu_arch"].startswith("gfx950") and len(pv["sources_sha256"]) == 16
+        assert d["parity"]["rows"] == 64 and d["parity"]["pass"] is True
+        assert d["metric"].startswith("attention fwd TFLOP/s (bf16, causal)")
+        ck = d["clock"]
+        assert ck["mean_mhz"] is None or 100 < ck["mean_mhz"] < 3000
 
 
 @pytest.mark.gpu
@@ -81,3 +89,16 @@ def test_forward_roofline_choice_and_formulas():
             assert r["unit"] == "TFLOP/s" and abs(r["achieved"] - f / 1e-3 / 1e12) < 1e-6 * r["achieved"]
         else:
             assert r["unit"] == "GB/s" and abs(r["achieved"] - cb / 1e-3 / 1e9) < 1e-6 * r["achieved"]
+
+
+def test_clock_sampler_without_a_gpu_reports_no_clock():
+    """Where amdsmi sees no GPU the sampler records why and reports no clock (never raises)."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    with bench.ClockSampler() as c:
+        pass
+    r = c.result(1000.0)
+    assert set(r) >= {"source", "samples", "mean_mhz", "error"}
+    if not r["samples"]:
+        assert r["mean_mhz"] is None and r["error"]

@@ -66,9 +66,35 @@ def test_small_configs_full(name):
     full_case(w.B, w.H, w.N, w.d, w.causal, w.seed, w.dist)
 
 
-@pytest.mark.parametrize("name", ["C3", "C4", "C5", "C4-shard"])
+@pytest.mark.parametrize("name", ["C3", "C5"])
+def test_large_configs_every_row(name):
+    """Full-size launch in the benchmark's launch shape, every output row of every head against
+    the float64 oracle (one head at a time, so the score matrix stays one head's size); the
+    max-abs and mean-abs bars apply to all B*H*N*d outputs together."""
+    w = W.by_name(name)
+    q, k, v = W.make_workload_inputs(w)
+    scale = W.fp32_scale(w.d)
+    say(f"{name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} dist={w.dist}, every row")
+    o, lse = run_gpu(q, k, v, w.causal, scale)
+    o_np, lse_np = o.double().numpy(), lse.double().numpy()
+    assert np.isfinite(o_np).all() and np.isfinite(lse_np).all(), f"{name}: non-finite output"
+    err_max = err_sum = lerr_max = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            ho, hl = attention_fp64(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
+                                    causal=w.causal, scale=scale)
+            e = np.abs(o_np[b:b + 1, h:h + 1] - ho)
+            err_max, err_sum = max(err_max, float(e.max())), err_sum + float(e.sum())
+            lerr_max = max(lerr_max, float(np.abs(lse_np[b:b + 1, h:h + 1] - hl).max()))
+    err_mean = err_sum / o_np.size
+    say(f"{name} every row: O max {err_max:.3e} mean {err_mean:.3e}  LSE max {lerr_max:.3e}")
+    assert err_max <= O_MAX and err_mean <= O_MEAN and lerr_max <= LSE_MAX, name
+
+
+@pytest.mark.parametrize("name", ["C4", "C4-shard"])
 def test_large_configs_sampled(name):
-    """Full-size launch; every row of two heads plus 256 seeded sampled rows checked."""
+    """Full-size launch; 256 seeded sampled rows checked (the oracle of every row of the
+    16,384-long heads would take minutes of host time)."""
     w = W.by_name(name)
     q, k, v = W.make_workload_inputs(w)
     scale = W.fp32_scale(w.d)
@@ -79,11 +105,6 @@ def test_large_configs_sampled(name):
     r = rows.numpy()
     check(o[r[:, 0], r[:, 1], r[:, 2]].double().numpy(), lse[r[:, 0], r[:, 1], r[:, 2]].double().numpy(), ro, rl,
           f"{name} 256 sampled rows")
-    if w.N <= 4096:
-        for (b, h) in ((0, 0), (w.B - 1, w.H - 1)):
-            ho, hl = attention_fp64(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1],
-                                    causal=w.causal, scale=scale)
-            check(o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], ho, hl, f"{name} head ({b},{h})")
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
@@ -143,9 +164,10 @@ def test_growing_maximum_forces_rescales():
     g = torch.Generator().manual_seed(3)
     v = torch.randn(1, 2, N, d, generator=g)
     q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    c = float(np.float32(0.08))  # the float32 value the library receives (reading R5)
     for causal in (False, True):
-        o, lse = run_gpu(q, k, v, causal, 0.08)
-        ro, rl = attention_fp64(q, k, v, causal=causal, scale=0.08)
+        o, lse = run_gpu(q, k, v, causal, c)
+        ro, rl = attention_fp64(q, k, v, causal=causal, scale=c)
         check(o, lse, ro, rl, f"growing max causal={causal}")
 
 
@@ -191,6 +213,7 @@ def test_zero_logits_average_v(causal):
 def test_negative_and_odd_scales(d):
     q, k, v = W.make_inputs(1, 2, 333, d, seed=15)
     for scale in (-0.2, 0.5, 1e-3, -1.0 / math.sqrt(d)):
+        scale = float(np.float32(scale))  # the float32 value the library receives (reading R5)
         for causal in (False, True):
             o, lse = run_gpu(q, k, v, causal, scale)
             ro, rl = attention_fp64(q, k, v, causal=causal, scale=scale)

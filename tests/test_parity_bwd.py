@@ -60,7 +60,7 @@ def case(B, H, Nq, Nk, d, causal, seed, scale=None, dist="normal", end_to_end=Fa
 
     q, k, v = W.make_rect_inputs(B, H, Nq, Nk, d, seed, dist)
     do = W.make_grad_output(B, H, Nq, d, seed)
-    scale = W.fp32_scale(d) if scale is None else scale
+    scale = W.fp32_scale(d) if scale is None else float(np.float32(scale))  # as the library receives it
     what = f"B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal} seed={seed} scale={scale:g} e2e={end_to_end}"
     say(what)
     rdq, rdk, rdv, rlse = attention_bwd_fp64(q, k, v, do, causal=causal, scale=scale)

@@ -93,7 +93,7 @@ def test_splitkv_workspace_reuse_and_determinism():
     o2, l2 = run(binding.attention_splitkv, q2, k2, v2, False, 0.2, workspace=ws)
     o3, l3 = run(binding.attention_splitkv, q, k, v, True, 0.1, workspace=ws)
     assert torch.equal(o1, o3) and torch.equal(l1, l3)
-    ro, rl = attention_fp64(q2, k2, v2, causal=False, scale=0.2)
+    ro, rl = attention_fp64(q2, k2, v2, causal=False, scale=float(np.float32(0.2)))
     check(o2, l2, ro, rl, "second call, smaller shape, same workspace")
 
 

@@ -136,7 +136,7 @@ def test_custom_op_autograd(layout, causal):
     assert o.dtype == torch.bfloat16 and o.shape == (B, H, N, d)
     o.backward(do.cuda() if layout == "bhnd" else do.transpose(1, 2).contiguous().cuda().transpose(1, 2))
     torch.cuda.synchronize()
-    scale = 1.0 / np.sqrt(d)
+    scale = W.fp32_scale(d)  # the float32 value the library receives (reading R5)
     ro, rl = attention_fp64(q, k, v, causal=causal, scale=scale)
     check_o(o, None, ro, rl, f"sdpa {layout} causal={causal}", True)
     grads = [t.grad if layout == "bhnd" else t.grad.transpose(1, 2) for t in leaves]
@@ -159,9 +159,10 @@ def test_custom_op_lower_right_and_mqa():
     o.backward(do.cuda())
     torch.cuda.synchronize()
     ek, ev = k1.expand(B, H, Nk, d), v1.expand(B, H, Nk, d)
-    ro, rl = attention_fp64(q, ek, ev, causal=True, scale=0.2)
+    c = float(np.float32(0.2))  # the float32 value the library receives (reading R5)
+    ro, rl = attention_fp64(q, ek, ev, causal=True, scale=c)
     check_o(o, None, ro, rl, "sdpa lower-right + one kv head", True)
-    rdq, rdk, rdv, _ = attention_bwd_fp64(q, ek, ev, do, causal=True, scale=0.2)
+    rdq, rdk, rdv, _ = attention_bwd_fp64(q, ek, ev, do, causal=True, scale=c)
     # the shared head's gradient is the sum over the query heads
     check_grads((tq.grad, tk.grad, tv.grad), (rdq, rdk.sum(axis=1, keepdims=True), rdv.sum(axis=1, keepdims=True)),
                 "sdpa one kv head", True)

@@ -50,6 +50,7 @@ def run(x, scale, out=None, with_lse=True):
 
 def full_case(rows, cols, dtype, std, seed, scale=1.0):
     x = W.make_softmax_input(rows, cols, dtype, std, seed)
+    scale = float(np.float32(scale))  # the float32 value the library receives
     say(f"rows={rows} cols={cols} dtype={dtype} std={std} seed={seed} scale={scale}")
     y, lse = run(x.cuda(), scale)
     yr, lr = softmax_rows_fp64(x, scale)
@@ -118,8 +119,10 @@ def test_masked_entries(dtype, cols):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("cols", [64, 4096, 16384, 20000])
+@pytest.mark.parametrize("cols", [64, 4096, 16384, 20000, 65536, 140000])
 def test_in_place_and_no_lse(dtype, cols):
+    """y = x: every launch shape, including the 1024-thread resident rows (65,536) and the
+    streamed rows (140,000: two passes over x, the second writing over it)."""
     x = W.make_softmax_input(6, cols, dtype, 2.0, seed=21)
     yr, lr = softmax_rows_fp64(x, 0.5)
     d = x.cuda()

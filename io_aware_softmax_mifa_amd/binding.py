@@ -13,7 +13,8 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmifa.so")
+# MIFA_LIBRARY may name another build of the same library (the host-ASan test build).
+_LIB_PATH = os.environ.get("MIFA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmifa.so")
 
 MIFA_OK = 0
 STATUS_NAMES = {

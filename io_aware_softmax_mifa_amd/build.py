@@ -39,6 +39,35 @@ def flags(extra=()):
     ]
 
 
+def build_host_asan(out_dir: str, verbose: bool = False) -> str:
+    """The same library with AddressSanitizer on the host code only (argument checks, launch
+    set-up); the device code is unchanged.  For CPU tests of the C ABI: load it into a process
+    started with the ASan runtime preloaded (asan_runtime())."""
+    os.makedirs(out_dir, exist_ok=True)
+    out = os.path.join(out_dir, "libmifa.so")
+    asan = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libsan"]
+    cmd = [hipcc(), *flags(asan), *SOURCES, "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, cwd=out_dir, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc (host ASan) failed ({res.returncode}):\n{res.stderr}")
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def asan_runtime() -> str:
+    """Path of the clang ASan runtime matching hipcc's host compiler."""
+    clang = os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin", "clang")
+    for cand in (clang, "/opt/rocm/lib/llvm/bin/clang", shutil.which("clang")):
+        if cand and os.path.exists(cand):
+            r = subprocess.run([cand, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+            path = r.stdout.strip()
+            if r.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+    raise RuntimeError("clang ASan runtime not found")
+
+
 def build(verbose: bool = False, save_temps: str | None = None) -> str:
     extra = []
     if save_temps:

@@ -71,14 +71,16 @@ namespace {
 using namespace mifa_detail;
 
 constexpr int kRowsPerWave = 32;
-constexpr int kMaxBR = 256;                 // largest workgroup row tile (8 waves)
 constexpr float kRescaleSlack = 8.0f;       // log2 units: weights stay <= 2^8 between rescales
 
 // ---- tile geometry -----------------------------------------------------------------------------
-template <int D_, int BC_, int WAVES_, int NBUF_>
+// GROUPS_ = 2: the waves form two groups that share the rows and split the key blocks (even
+// blocks to group 0, odd ones to group 1); their partial results merge at the end.
+template <int D_, int BC_, int WAVES_, int NBUF_, int GROUPS_ = 1>
 struct Cfg {
-  static constexpr int D = D_, BC = BC_, WAVES = WAVES_, NBUF = NBUF_;
-  static constexpr int kBR = WAVES * kRowsPerWave;         // query rows per workgroup
+  static constexpr int D = D_, BC = BC_, WAVES = WAVES_, NBUF = NBUF_, kGroups = GROUPS_;
+  static constexpr int kWavesPerGroup = WAVES / kGroups;
+  static constexpr int kBR = kWavesPerGroup * kRowsPerWave;  // query rows per workgroup
   static constexpr int kThreads = WAVES * 64;
   static constexpr int kChunksPerRow = D / 8;              // 16-byte chunks per K/V row
   static constexpr int kRowsPerInst = 64 / kChunksPerRow;  // rows one wave-wide DMA covers
@@ -97,6 +99,7 @@ struct Cfg {
   static_assert(kInstPerTensor % WAVES == 0 && kInstPerWave >= 1, "block must split evenly over the waves");
   static_assert(BC % 32 == 0, "key block must be a multiple of the 32-key MFMA tile");
   static_assert(NBUF == 2 || NBUF == 4, "two or four K/V buffers");
+  static_assert(kGroups == 1 || (kGroups == 2 && NBUF == 4 && WAVES == 8), "key-split groups: 8 waves, 4 buffers");
   static constexpr int kUnroll = NBUF % 2 == 0 ? NBUF : 2 * NBUF;  // blocks per loop trip
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget of one workgroup");
   static_assert((NBUF - 1) * kTensorBytes + (kKT - 1) * 32 * D * 2 <= 65535, "K read immediates fit in 16 bits");
@@ -462,7 +465,8 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
   Wave<C, CAUSAL> W;
   const int N = Nk - key_base;
   W.N = N;
-  W.row0 = qt * kBR + wave * kRowsPerWave;
+  const int grp = wave / C::kWavesPerGroup;  // key-split group (0 unless kGroups == 2)
+  W.row0 = qt * kBR + (wave - grp * C::kWavesPerGroup) * kRowsPerWave;
   W.my_row = W.row0 + ln;
   W.my_pos = W.my_row + kshift - key_base;
   // Key blocks this wave needs: with the causal mask, up to the last visible key of its last
@@ -518,7 +522,61 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
 
   f32x16 sA[C::kKT], sB[C::kKT];
   const int last = nblk - 1;
-  if constexpr (NBUF == 4) {
+  if constexpr (C::kGroups == 2) {
+    // ---- two groups of four waves over the same 128 rows, one barrier per two blocks ----
+    // Group g runs the blocks j = g, g+2, g+4, ...; between two barriers group 0 runs block j and
+    // group 1 block j+1 (j even), side by side, so each wave walks half of the key blocks.  K(i)
+    // lives in K buffer i % 4 and V(i) in V buffer i % 4.  The period from the barrier before
+    // block j reads K(j+2), K(j+3) (the next scores of the two groups) and V(j), V(j+1); right
+    // after that barrier the waves of group 0 issue K(j+4), K(j+5), V(j+2), V(j+3), their share
+    // and that of the group-1 wave on their SIMD, into the buffers the previous period read.
+    auto ld = [&](int blk, int w, const unsigned (&odk)[C::kInstPerWave], const unsigned (&odv)[C::kInstPerWave],
+                  bool is_v) {
+      if (blk > last) return;
+      if (is_v)
+        issue_one<C, true>(vh, smem, blk, blk % NBUF, N, w, lane, W.la, odv);
+      else
+        issue_one<C, false>(kh, smem, blk, blk % NBUF, N, w, lane, W.la, odk);
+    };
+    auto both = [&](int blk, bool is_v) {
+      ld(blk, wave, W.la.dk, W.la.dv, is_v);
+      ld(blk, wave + C::WAVES / 2, W.la.pdk, W.la.pdv, is_v);
+    };
+    // Prologue, every wave its own share: K(0) .. K(3), V(0), V(1).
+    for (int b = 0; b < 4; ++b) ld(b, wave, W.la.dk, W.la.dv, false);
+    ld(0, wave, W.la.dk, W.la.dv, true);
+    ld(1, wave, W.la.dk, W.la.dv, true);
+    // Group 0 always reads an even buffer and group 1 the next one, so group 1's LDS read
+    // addresses start one buffer further and both groups run the same code.
+    if (grp == 1) {
+      W.la.k += C::kTensorBytes;
+#pragma unroll
+      for (int s = 0; s < C::kDS; ++s) W.la.ka[s] += C::kTensorBytes;
+#pragma unroll
+      for (int t = 0; t < C::kDT; ++t) W.la.v[t] += C::kTensorBytes;
+    }
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    W.first_scores(sA);
+    // Period U2 of a trip of two periods (four blocks): group g runs block j0 + 2 U2 + g, whose
+    // scores were computed into cur and whose next scores (block + 2) go to nxt.
+    auto period = [&]<int U2>(int j, f32x16(&cur)[C::kKT], f32x16(&nxt)[C::kKT], IC<U2>) {
+      wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      if (grp == 0) {
+        both(j + 4, false);
+        both(j + 2, true);
+        both(j + 5, false);
+        both(j + 3, true);
+      }
+      const int jb = j + grp;
+      if (jb < nblk_w) W.template block<(2 * U2 + 2) % NBUF, (2 * U2) % NBUF>(cur, nxt, jb * BC, jb >= j_mask);
+    };
+    for (int j0 = 0; j0 < nblk; j0 += 4) {
+      period(j0, sA, sB, IC<0>{});
+      if (j0 + 2 < nblk) period(j0 + 2, sB, sA, IC<1>{});
+    }
+  } else if constexpr (NBUF == 4) {
     // ---- DMA schedule: one barrier per two blocks ----
     // K(i) lives in K buffer i % 4 and V(i) in V buffer i % 4.  Before every even block j all
     // waves meet at a barrier, and right after it the DMA of K(j+3), K(j+4), V(j+2), V(j+3)
@@ -621,9 +679,42 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
   // No load is left in flight when the workgroup's LDS is handed to another workgroup.
   wait_vmcnt<0>();
 
+  float l_tot = half_sum(W.l_run);
+  if constexpr (C::kGroups == 2) {
+    // ---- merge of the two groups' partial results (same rows, disjoint key blocks) ----
+    // Each holds O, the row sum l and the max m it was taken against; with m = max(m0, m1) the
+    // rows combine as O = 2^(m0-m) O0 + 2^(m1-m) O1 and l likewise (a partial with no visible
+    // key has m = -inf and weight 0).  Group 1 passes its values through LDS (the K/V buffers,
+    // free once every wave is past its last block); both waves of a pair hold the same rows
+    // in the same lane layout, so the exchange is element by element.
+    constexpr int kVals = C::kDT * 16 + 2;
+    static_assert(C::kWavesPerGroup * kVals * 64 * 4 <= C::kLdsBytes, "merge buffer fits the K/V buffers");
+    float* xch = (float*)smem + (wave - grp * C::kWavesPerGroup) * kVals * 64 + lane;
+    __syncthreads();  // every wave is done reading K and V
+    if (grp == 1) {
+#pragma unroll
+      for (int t = 0; t < C::kDT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xch[(16 * t + i) * 64] = W.oacc[t][i];
+      xch[(kVals - 2) * 64] = W.m_run;
+      xch[(kVals - 1) * 64] = l_tot;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = xch[(kVals - 2) * 64], l1 = xch[(kVals - 1) * 64];
+    const float m = fmax2(W.m_run, m1);
+    const float a0 = W.m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(W.m_run - m);
+    const float a1 = m1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+    for (int t = 0; t < C::kDT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) W.oacc[t][i] = a0 * W.oacc[t][i] + a1 * xch[(16 * t + i) * 64];
+    l_tot = a0 * l_tot + a1 * l1;
+    W.m_run = m;
+  }
+
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l) ----
   // (A row with no visible key in this workgroup's key range has l = 0: O = 0, LSE = -inf.)
-  const float l_tot = half_sum(W.l_run);
   if (W.my_row < Nq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     const int64_t orow = o_off + W.my_row * p.o_sn;
@@ -725,7 +816,7 @@ hipError_t launch(const Problem& pr, hipStream_t stream) {
   // workgroup then has n+1 key blocks, and half as many workgroups are dispatched.  Measured
   // on MI355X (same-box A/B, medians, identical output): B=2 H=16 N=4096 -4.8%, B=8 H=16 N=2048
   // -0.9%, B=1 H=32 N=16384 -0.6%.
-  constexpr bool kCanPair = CAUSAL && C::WAVES == 8;
+  constexpr bool kCanPair = CAUSAL && C::WAVES == 8 && C::kGroups == 1;
   const bool pair = kCanPair && pr.n_splits == 1 && p.n_qtiles > 1;
   const int64_t grid = (int64_t)pr.BH * (pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles) * pr.n_splits;
   auto kern = mifa_fwd_kernel<C, CAUSAL, false>;
@@ -741,7 +832,8 @@ hipError_t launch(const Problem& pr, hipStream_t stream) {
 }
 
 // Launch-shape choice: 8-wave workgroups (256 rows, one per CU) for sequences longer than 1024
-// with more of them than CUs; otherwise 4-wave workgroups (128 rows, two per CU).  Measured on
+// with more of them than CUs; 8-wave workgroups with two key-split groups (128 rows) for few
+// tiles; otherwise 4-wave workgroups (128 rows, two per CU).  Measured on
 // MI355X (same-box A/B): with 8 waves B=1 H=32 N=16384 causal runs ~8 % faster, B=2 H=16
 // N=4096 causal ~7 % and B=8 H=16 N=2048 causal ~3 %; with exactly one 256-row tile per CU
 // (B=1 H=4 N=16384, B=1 H=8 N=8192) 4 waves are 1-2.5 % faster, since two workgroups per CU
@@ -751,7 +843,14 @@ constexpr int kLongN = 1024;
 template <int D, bool CAUSAL>
 hipError_t dispatch(const Problem& pr, hipStream_t stream) {
   const int64_t big_tiles = (int64_t)pr.BH * ((pr.Nq + 255) / 256);
+  const int64_t tiles = (int64_t)pr.BH * ((pr.Nq + 127) / 128);
   if (pr.n_splits == 1 && pr.Nq > kLongN && big_tiles > kCUs) return launch<Cfg<D, 64, 8, 4>, CAUSAL>(pr, stream);
+  // Few 128-row tiles (at most one per CU) over at least 512 keys: two groups of four waves per
+  // tile split the key blocks, so twice as many waves share the work of a tile.  Measured on
+  // MI355X (same-box A/B, medians): B=4 H=8 N=1024 d=64 -8% causal and non-causal against one
+  // 4-wave workgroup per tile; N=128 (one tile, two key blocks) +15%, and with 512 tiles, where
+  // 4-wave workgroups fit twice per CU, +13%, so those keep the 4-wave launch.
+  if (pr.n_splits == 1 && tiles <= kCUs && pr.Nk >= 512) return launch<Cfg<D, 64, 8, 4, 2>, CAUSAL>(pr, stream);
   return launch<Cfg<D, 64, 4, 2>, CAUSAL>(pr, stream);
 }
 

@@ -131,6 +131,40 @@ def test_long_sequence_launch_shape(d, causal, dist):
           f"long d={d} causal={causal} {dist} sampled rows")
 
 
+# ---- the key-split launch (few tiles: two wave groups per tile share the key blocks) --------
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [512, 777, 1000, 2113])
+def test_key_split_launch(N, d, causal):
+    """At most one 128-row tile per CU and at least 512 keys: two groups of waves take the even
+    and odd key blocks of a tile and merge at the end.  Odd and even block counts, partial last
+    blocks, causal diagonals inside either group's blocks; every row of every head checked, on
+    NaN-filled outputs."""
+    B, H = 1, 3
+    q, k, v = W.make_inputs(B, H, N, d, seed=5000 + N + d, dist="stress" if N == 777 else "normal")
+    scale = W.fp32_scale(d)
+    say(f"key split: B={B} H={H} N={N} d={d} causal={causal}")
+    o, lse = run_gpu(q, k, v, causal, scale, poison=True)
+    ro, rl = attention_fp64(q, k, v, causal=causal, scale=scale)
+    check(o, lse, ro, rl, f"key split N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_key_split_launch_rectangular(d):
+    """Few queries against many keys through mifa_attention (no key-range partials): the newest
+    70 positions of 2,500 with the causal mask, and without it."""
+    from io_aware_softmax_mifa_amd import binding
+
+    q, k, v = W.make_rect_inputs(2, 2, 70, 2500, d, seed=5100 + d)
+    scale = W.fp32_scale(d)
+    for causal in (False, True):
+        o, lse = binding.attention(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        ro, rl = attention_fp64(q, k, v, causal=causal, scale=scale)
+        check(o.cpu(), lse.cpu(), ro, rl, f"key split rect d={d} causal={causal}")
+
+
 # ---- ragged and tiny sequence lengths --------------------------------------------------
 
 @pytest.mark.parametrize("d", [64, 128])

@@ -23,8 +23,8 @@ compulsory bytes (the input read once, the output and the row LSE written once).
 
 Besides the driver's fields, `roofline` and `cpu_baseline`, the line carries `provenance` (source
 hashes, git commit where available, GPU, ROCm/HIP/torch versions, seed); on the attention legs
-`clock`, the sustained engine clock sampled with amdsmi over a further second of untimed
-launches after the timed ones and the percentage of the peak at that clock; and on the forward
+`clock`, the sustained engine clock measured on the GPU by mifa_clock_probe during a further
+second of untimed launches after the timed ones, and the percentage of the peak at that clock; and on the forward
 legs `parity`, the errors of the last timed launch's O and LSE on the rows the CPU-baseline leg
 computed with the float64 oracle.
 """
@@ -159,29 +159,76 @@ def host_info() -> dict:
 
 
 PEAK_CLOCK_MHZ = 2400.0    # MI355X peak engine clock, the clock the 2.5 PFLOP/s figure assumes
-CLOCK_WINDOW_S = 1.0       # untimed launches after the timed steps, during which the clock is sampled
+CLOCK_WINDOW_S = 1.0       # untimed launches after the timed steps, during which the clock is measured
+CLOCK_SETTLE_S = 0.25      # into that window, when the clock probe starts
+CLOCK_SPAN_US = 500_000    # the probe's span
 
 
 def sample_clock(step, value_tflops):
-    """The sustained engine clock under this workload: launches of the same step for about
-    CLOCK_WINDOW_S seconds after the timed region (untimed, not part of `value`), sampled with
-    amdsmi.  Returns the ClockSampler report with the clock-adjusted peak."""
+    """The sustained engine clock under this workload, measured on the GPU.  After the timed
+    region (untimed, not part of `value`) the same step keeps running for CLOCK_WINDOW_S
+    seconds; CLOCK_SETTLE_S into that window mifa_clock_probe starts 8 single-wave probes on a
+    second stream, which read the shader-clock and real-time counters CLOCK_SPAN_US apart.
+    Returns the per-probe clocks and, for a compute-bound leg, the bf16 peak scaled to their
+    median and `value_tflops` as a percentage of it."""
     import torch
 
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < CLOCK_WINDOW_S:
-            for _ in range(50):
-                step()
-            torch.cuda.synchronize()
-    return clock.result(value_tflops)
+    from io_aware_softmax_mifa_amd import binding
+
+    out = {"source": (f"mifa_clock_probe: 8 single-wave probes on a second stream read s_memtime and "
+                      f"s_memrealtime {CLOCK_SPAN_US / 1e3:g} ms apart, starting {CLOCK_SETTLE_S:g} s into "
+                      f"{CLOCK_WINDOW_S:g} s of further launches of the same step after the timed steps"),
+           "probe_mhz": None, "median_mhz": None, "min_mhz": None, "max_mhz": None, "error": None}
+    buf = torch.zeros(32, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()  # default priority; non-blocking with respect to the null stream
+    khz, launched, prev = 0, None, None
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < CLOCK_WINDOW_S:
+        for _ in range(20):
+            step()
+        ev = torch.cuda.Event()
+        ev.record()
+        if prev is not None:
+            prev.synchronize()  # keep about one chunk queued behind the running one
+        prev = ev
+        if launched is None and time.perf_counter() - t0 >= CLOCK_SETTLE_S:
+            st, khz = binding.mifa_clock_probe_raw(buf, CLOCK_SPAN_US, side.cuda_stream)
+            launched = time.perf_counter() - t0
+            if st != 0:
+                out["error"] = f"mifa_clock_probe: {binding.mifa_status_string(st)}"
+                break
+    torch.cuda.synchronize()
+    if out["error"] is None and launched is None:
+        out["error"] = "the probe was not launched"
+    if out["error"] is None and CLOCK_WINDOW_S - launched < CLOCK_SPAN_US * 1e-6:
+        out["error"] = "the step stopped before the probe's span ended"
+    if out["error"] is None:
+        v = buf.cpu().tolist()
+        mhz = []
+        for w in range(8):
+            dt, dr = v[4 * w + 2] - v[4 * w], v[4 * w + 3] - v[4 * w + 1]
+            mhz.append(dt / dr * khz / 1e3 if dr > 0 else float("nan"))
+        out["probe_mhz"] = [round(x, 1) for x in mhz]
+        if not all(100.0 < x < 3000.0 for x in mhz):
+            out["error"] = "probe clock outside 100..3000 MHz"
+        else:
+            srt = sorted(mhz)
+            out.update(median_mhz=srt[len(srt) // 2], min_mhz=srt[0], max_mhz=srt[-1])
+            if value_tflops is not None:
+                peak = PEAK_BF16_TFLOPS * out["median_mhz"] / PEAK_CLOCK_MHZ
+                out["clock_adjusted_peak_tflops"] = peak
+                out["pct_of_clock_adjusted_peak"] = 100.0 * value_tflops / peak
+    return out
+
+
 SOURCES = [os.path.join(ROOT, "io_aware_softmax_mifa_amd", "csrc", f)
-           for f in ("mifa_fwd.hip", "mifa_bwd.hip", "mifa_softmax.hip", "mifa_common.h")]
+           for f in ("mifa_fwd.hip", "mifa_bwd.hip", "mifa_softmax.hip", "mifa_clock.hip", "mifa_common.h")]
 
 
 def provenance(seed) -> dict:
     """What produced this line: source hashes, git commit (where the checkout has .git), GPU and
-    software versions, and the workload's seed."""
+    software versions, and the workload's seed.  The GPU's name is amdsmi's market name, else
+    the HIP device name (which can be a generic one)."""
     import subprocess
 
     import torch
@@ -202,94 +249,26 @@ def provenance(seed) -> dict:
     except OSError:
         pass
     props = torch.cuda.get_device_properties(0)
+    name = None
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
+        try:
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if handles:
+                name = amdsmi.amdsmi_get_gpu_asic_info(handles[0]).get("market_name") or None
+        finally:
+            amdsmi.amdsmi_shut_down()
+    except Exception:  # noqa: BLE001 -- the name is informational
+        name = None
+    name = name or torch.cuda.get_device_name(0) or None
     from io_aware_softmax_mifa_amd import binding
 
-    return {"git_sha": sha, "sources_sha256": h.hexdigest()[:16], "gpu_name": torch.cuda.get_device_name(0),
+    return {"git_sha": sha, "sources_sha256": h.hexdigest()[:16], "gpu_name": name,
             "gpu_arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
             "rocm_version": rocm, "hip_runtime": torch.version.hip, "torch_version": torch.__version__,
             "library": binding.mifa_version(), "seed": seed}
-
-
-class ClockSampler:
-    """Samples the GPU engine clock with amdsmi on a background thread (the launches are queued
-    asynchronously, so the thread does not delay the GPU).  The driver refreshes the clock it
-    reports only every few milliseconds, so the sampler is run over a window of about a second;
-    samples from the first `skip_s` seconds (the clock still settling) are dropped.  Reports the
-    mean over the kept samples, or None where amdsmi is unavailable."""
-
-    def __init__(self, period_s: float = 0.005, skip_s: float = 0.25):
-        self.period_s, self.skip_s, self.samples, self.error = period_s, skip_s, [], None
-
-    def _read(self):
-        import amdsmi
-
-        m = amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
-        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and 0 < c < 10000]
-        if clks:
-            return sum(clks) / len(clks)
-        c = m.get("current_gfxclk")
-        if isinstance(c, (int, float)) and 0 < c < 10000:
-            return float(c)
-        return float(amdsmi.amdsmi_get_clock_info(self.handle, amdsmi.AmdSmiClkType.SYS)["clk"])
-
-    def _loop(self):
-        t0 = time.perf_counter()
-        while not self.stop:
-            try:
-                c = self._read()
-                if time.perf_counter() - t0 >= self.skip_s:
-                    self.samples.append(c)
-            except Exception as e:  # noqa: BLE001 -- a sampling failure only loses the clock figure
-                self.error = repr(e)
-                return
-            time.sleep(self.period_s)
-
-    def __enter__(self):
-        import threading
-
-        self.stop, self.thread = False, None
-        try:
-            import amdsmi
-
-            amdsmi.amdsmi_init(amdsmi.AmdSmiInitFlags.INIT_AMD_GPUS)
-            handles = amdsmi.amdsmi_get_processor_handles()
-            if len(handles) != 1:
-                raise RuntimeError(f"{len(handles)} GPUs visible to amdsmi; the clock would be ambiguous")
-            self.handle = handles[0]
-            self._read()
-            self.thread = threading.Thread(target=self._loop, daemon=True)
-            self.thread.start()
-        except Exception as e:  # noqa: BLE001
-            self.error = repr(e)
-        return self
-
-    def __exit__(self, *exc):
-        self.stop = True
-        if self.thread is not None:
-            self.thread.join()
-        try:
-            import amdsmi
-
-            amdsmi.amdsmi_shut_down()
-        except Exception:  # noqa: BLE001
-            pass
-        return False
-
-    def result(self, tflops: float | None = None) -> dict:
-        out = {"source": ("amdsmi gpu_metrics current_gfxclks (mean over XCDs per sample; the peak uses the median over samples), sampled every "
-                          f"{1e3 * self.period_s:g} ms over {CLOCK_WINDOW_S:g} s of further launches of the same "
-                          f"step after the timed steps, the first {self.skip_s:g} s dropped"),
-               "samples": len(self.samples), "mean_mhz": None, "min_mhz": None, "max_mhz": None,
-               "error": self.error}
-        if self.samples:
-            srt = sorted(self.samples)
-            out.update(mean_mhz=sum(srt) / len(srt), median_mhz=srt[len(srt) // 2], min_mhz=srt[0], max_mhz=srt[-1])
-            if tflops is not None:
-                # the median: samples that catch XCDs idle between launches would pull a mean down
-                peak = PEAK_BF16_TFLOPS * out["median_mhz"] / PEAK_CLOCK_MHZ
-                out["clock_adjusted_peak_tflops"] = peak
-                out["pct_of_clock_adjusted_peak"] = 100.0 * tflops / peak
-        return out
 
 
 def event_stats(starts, ends) -> dict:

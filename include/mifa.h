@@ -19,11 +19,14 @@
  *
  * Conventions for every entry point:
  *   - Pointers named q, k, v, o, lse, x, y are DEVICE pointers (hipMalloc'd or equivalent) on
- *     the current HIP device.  The caller allocates and owns them; the library allocates
- *     nothing and keeps no pointer after returning.  Its only state across calls is the
- *     per-thread code read by mifa_last_hip_error and, per kernel, an atomic record of the
- *     devices on which that kernel's dynamic-LDS limit has already been raised (set on its
- *     first launch there); calls are thread-safe and re-entrant.
+ *     the current HIP device.  The caller allocates and owns them; the library calls no
+ *     allocator and keeps no caller pointer after returning.  Its state across calls is the
+ *     per-thread code read by mifa_last_hip_error; per kernel, an atomic record of the devices
+ *     on which that kernel's dynamic-LDS limit has already been raised (set on its first
+ *     launch there); and, for mifa_attention_splitkv_noalloc only, a 32 MiB device array held
+ *     by each GPU the library runs on, with its device address cached per device on first
+ *     use.  Calls are thread-safe and re-entrant (the one exception, overlapping calls of
+ *     mifa_attention_splitkv_noalloc on one GPU, is stated at that entry point).
  *   - `stream` is a hipStream_t passed as void*; NULL means the null stream.  Work is
  *     enqueued asynchronously on it and the library never synchronises.  The caller must
  *     keep every buffer alive and unmodified until the stream has passed the kernel.
@@ -258,6 +261,31 @@ int64_t mifa_bwd_workspace_bytes(int64_t B, int64_t H, int64_t Nq);
  */
 int mifa_softmax_rows(const void* x, void* y, float* lse, int64_t rows, int64_t cols, int dtype,
                       float scale, void* stream);
+
+/*
+ * mifa_clock_probe -- measures the engine clock the GPU sustains while other work runs
+ * (a measurement aid, not part of the attention path).  Roofline fractions of the
+ * compute-bound kernels are quoted against the bf16 MFMA peak at the nominal 2.4 GHz clock;
+ * the fraction of the peak at the clock actually sustained separates the kernel's share of
+ * the gap from the clock's.
+ *
+ * Launches 8 single-wave workgroups on `stream`.  Each reads the shader-clock counter
+ * (s_memtime, one count per engine-clock cycle) and the fixed-rate real-time counter
+ * (s_memrealtime) at its start, sleeps for span_us microseconds of real time, and reads both
+ * again.  Launch it on a second stream while the work to be measured keeps the GPU busy on
+ * another; the mean engine clock of probe w in MHz is
+ *     (out[4w+2] - out[4w+0]) / (out[4w+3] - out[4w+1]) * realtime_khz / 1000.
+ *   out          device pointer to 32 int64 values (8-byte aligned), overwritten when the
+ *                kernel has run: {memtime start, realtime start, memtime end, realtime end}
+ *                for each of the 8 probes.
+ *   span_us      1 .. 2,000,000.  Each probe also stops after a bounded number of sleeps,
+ *                so it ends even if the real-time counter were to stall.
+ *   realtime_khz host pointer; receives the real-time counter's rate (kHz) before the launch.
+ *   stream       hipStream_t (as void*); NULL for the null stream.
+ * Errors: MIFA_ERR_NULL_POINTER (out or realtime_khz NULL), MIFA_ERR_BAD_SHAPE (span_us out
+ * of range), MIFA_ERR_MISALIGNED, MIFA_ERR_HIP.
+ */
+int mifa_clock_probe(long long* out, int64_t span_us, int* realtime_khz, void* stream);
 
 /* Human-readable name of a status code; never NULL (unknown codes give "unknown status"). */
 const char* mifa_status_string(int status);

@@ -35,7 +35,8 @@ MIFA_DTYPE_BF16, MIFA_DTYPE_F32 = 0, 1
 EXPORTED = ("mifa_fwd", "mifa_attention", "mifa_attention_strided", "mifa_attention_splitkv",
             "mifa_attention_splitkv_noalloc",
             "mifa_splitkv_workspace_bytes", "mifa_bwd", "mifa_bwd_strided", "mifa_bwd_workspace_bytes",
-            "mifa_softmax_rows", "mifa_status_string", "mifa_version", "mifa_last_hip_error")
+            "mifa_softmax_rows", "mifa_clock_probe", "mifa_status_string", "mifa_version",
+            "mifa_last_hip_error")
 
 
 class MifaError(RuntimeError):
@@ -81,6 +82,8 @@ def _load() -> ctypes.CDLL:
     lib.mifa_softmax_rows.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 2 + [ctypes.c_int, ctypes.c_float,
                                                                                       ctypes.c_void_p]
     lib.mifa_softmax_rows.restype = ctypes.c_int
+    lib.mifa_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.POINTER(ctypes.c_int), ctypes.c_void_p]
+    lib.mifa_clock_probe.restype = ctypes.c_int
     lib.mifa_status_string.argtypes = [ctypes.c_int]
     lib.mifa_status_string.restype = ctypes.c_char_p
     lib.mifa_version.argtypes = []
@@ -156,6 +159,14 @@ def mifa_attention_splitkv_noalloc_raw(q, k, v, o, lse, B, H, Nq, Nk, d, causal,
     return int(_lib.mifa_attention_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), int(B), int(H),
                                                    int(Nq), int(Nk), int(d), 1 if causal else 0, float(scale),
                                                    stream or None))
+
+
+def mifa_clock_probe_raw(out, span_us, stream) -> tuple[int, int]:
+    """Launch the engine-clock probe on `stream`; returns (status, real-time counter rate in kHz).
+    `out`: 32 int64 on the device, filled when the probe has run."""
+    khz = ctypes.c_int(0)
+    st = int(_lib.mifa_clock_probe(_ptr(out), int(span_us), ctypes.byref(khz), stream or None))
+    return st, int(khz.value)
 
 
 def mifa_splitkv_workspace_bytes(B, H, Nq, Nk, d) -> int:

@@ -12,7 +12,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mifa_fwd.hip", "mifa_bwd.hip", "mifa_softmax.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("mifa_fwd.hip", "mifa_bwd.hip", "mifa_softmax.hip", "mifa_clock.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libmifa.so")
 ARCH = "gfx950"

@@ -23,7 +23,7 @@ def declared_functions():
 def test_header_declares_expected_api():
     assert declared_functions() == ["mifa_attention", "mifa_attention_splitkv", "mifa_attention_splitkv_noalloc",
                                     "mifa_attention_strided", "mifa_bwd",
-                                    "mifa_bwd_strided", "mifa_bwd_workspace_bytes", "mifa_fwd",
+                                    "mifa_bwd_strided", "mifa_bwd_workspace_bytes", "mifa_clock_probe", "mifa_fwd",
                                     "mifa_last_hip_error", "mifa_softmax_rows", "mifa_splitkv_workspace_bytes",
                                     "mifa_status_string", "mifa_version"]
 
@@ -194,6 +194,14 @@ def test_splitkv_noalloc_checks(lib):
     assert lib.mifa_splitkv_workspace_bytes(*big) > 32 << 20
     assert lib.mifa_attention_splitkv_noalloc_raw(A, A, A, A, A, *big, 1, 0.1, None) == 11
     assert "32 MiB" in lib.mifa_status_string(11)
+
+
+def test_clock_probe_checks(lib):
+    # null pointers, the span's range and alignment are checked before any HIP call
+    assert lib.mifa_clock_probe_raw(0, 1000, None) == (1, 0)
+    assert lib.mifa_clock_probe_raw(A, 0, None) == (2, 0)
+    assert lib.mifa_clock_probe_raw(A, 2_000_001, None) == (2, 0)
+    assert lib.mifa_clock_probe_raw(A + 4, 1000, None) == (4, 0)
 
 
 def test_splitkv_workspace_bytes(lib):

@@ -783,7 +783,7 @@ struct Problem {
 };
 
 template <typename C, bool CAUSAL>
-hipError_t launch(const Problem& pr, hipStream_t stream) {
+hipError_t launch(const Problem& pr, hipStream_t stream, bool pair_tiles = true) {
   FwdParams p;
   p.q = (const __bf16*)pr.q;
   p.k = (const __bf16*)pr.k;
@@ -815,9 +815,9 @@ hipError_t launch(const Problem& pr, hipStream_t stream) {
   // Causal 8-wave launches over the whole key range pair their tiles (n-1-r with r): every
   // workgroup then has n+1 key blocks, and half as many workgroups are dispatched.  Measured
   // on MI355X (same-box A/B, medians, identical output): B=2 H=16 N=4096 -4.8%, B=8 H=16 N=2048
-  // -0.9%, B=1 H=32 N=16384 -0.6%.
-  constexpr bool kCanPair = CAUSAL && C::WAVES == 8 && C::kGroups == 1;
-  const bool pair = kCanPair && pr.n_splits == 1 && p.n_qtiles > 1;
+  // -0.9%, B=1 H=32 N=16384 -0.6%.  The key-split launch pairs only when asked (`pair_tiles`).
+  constexpr bool kCanPair = CAUSAL && C::WAVES == 8;
+  const bool pair = kCanPair && pair_tiles && pr.n_splits == 1 && p.n_qtiles > 1;
   const int64_t grid = (int64_t)pr.BH * (pair ? (p.n_qtiles + 1) / 2 : p.n_qtiles) * pr.n_splits;
   auto kern = mifa_fwd_kernel<C, CAUSAL, false>;
   if constexpr (kCanPair) {
@@ -850,7 +850,15 @@ hipError_t dispatch(const Problem& pr, hipStream_t stream) {
   // MI355X (same-box A/B, medians): B=4 H=8 N=1024 d=64 -8% causal and non-causal against one
   // 4-wave workgroup per tile; N=128 (one tile, two key blocks) +15%, and with 512 tiles, where
   // 4-wave workgroups fit twice per CU, +13%, so those keep the 4-wave launch.
-  if (pr.n_splits == 1 && tiles <= kCUs && pr.Nk >= 512) return launch<Cfg<D, 64, 8, 4, 2>, CAUSAL>(pr, stream);
+  if (pr.n_splits == 1 && tiles <= kCUs && pr.Nk >= 512) return launch<Cfg<D, 64, 8, 4, 2>, CAUSAL>(pr, stream, false);
+  // Causal, longer than 1024, between one and two 128-row tiles per CU: the key-split launch over
+  // tile pairs (n-1-r, r) gives every CU one workgroup with the same n+1 key blocks, where
+  // 128-row tiles two per CU leave the causal triangle unbalanced.  Measured on MI355X
+  // (same-box A/B, medians, against 4-wave workgroups): B=1 H=4 N=16384 d=128 -28.5%,
+  // B=1 H=8 N=8192 -26% (d=64 -29%), B=1 H=16 N=4096 -23%; at N=1024 (B=4 H=16) +13%, so
+  // shorter sequences keep the 4-wave launch.
+  if (CAUSAL && pr.n_splits == 1 && pr.Nq > kLongN && tiles > kCUs && tiles <= 2 * kCUs)
+    return launch<Cfg<D, 64, 8, 4, 2>, CAUSAL>(pr, stream, true);
   return launch<Cfg<D, 64, 4, 2>, CAUSAL>(pr, stream);
 }
 

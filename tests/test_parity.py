@@ -151,6 +151,21 @@ def test_key_split_launch(N, d, causal):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,N", [(1, 24, 1536), (1, 19, 1900), (2, 9, 2000)])
+def test_key_split_tile_pairs(B, H, N, d):
+    """Causal, between one and two 128-row tiles per CU: the key-split launch over tile pairs
+    (n-1-r, r).  24 heads take the XCD-grouped order with an even tile count; 19 and 18 heads
+    the plain order with 15 and 16 tiles (15: the middle tile runs alone), ragged last tiles;
+    every row of every head checked, on NaN-filled outputs."""
+    q, k, v = W.make_inputs(B, H, N, d, seed=5200 + H + d)
+    scale = W.fp32_scale(d)
+    say(f"key split, tile pairs: B={B} H={H} N={N} d={d} causal=True")
+    o, lse = run_gpu(q, k, v, True, scale, poison=True)
+    ro, rl = attention_fp64(q, k, v, causal=True, scale=scale)
+    check(o, lse, ro, rl, f"key split pairs B={B} H={H} N={N} d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_key_split_launch_rectangular(d):
     """Few queries against many keys through mifa_attention (no key-range partials): the newest
     70 positions of 2,500 with the causal mask, and without it."""

@@ -20,7 +20,9 @@
 //    three buffers), computes S = Q K^T and dP = dO V^T, then P and dS, and accumulates
 //    dV^T += dO^T P and dK^T += Q^T dS.  Software-pipelined: the score arithmetic of one
 //    32-query tile runs beside the S and dP products of the next and the dV/dK products of
-//    the previous one.
+//    the previous one.  With the causal mask, dkdv_split instead: 8 waves, the two waves of a
+//    SIMD sharing 32 keys in two roles (one computes S, P and dV, the other dP, dS and dK,
+//    with P passed through LDS), so two waves per SIMD overlap each other's arithmetic.
 // In both, the probabilities / dS feed the second product straight from the accumulator
 // layout (the contraction index inside one MFMA is a free permutation), as in the forward.
 #include <hip/hip_runtime.h>
@@ -735,6 +737,206 @@ constexpr int kRowValsBytes = 3 * 512;
 template <int D>
 constexpr int kDkdvLds = 6 * Geo<D>::kTile + kRowValsBytes;
 
+// ---- dK/dV with the two waves of each SIMD in two roles -------------------------------------
+// 8 waves, 128 keys per workgroup (256 registers per wave, two waves per SIMD).  Waves g and
+// g + 4 share a SIMD and the 32 keys 32 g .. 32 g + 31:
+//  * wave g keeps K: S = Q K^T, P = exp2(c S - LSE2) (masked scores give 0), P to LDS as bf16
+//    for its partner, dV^T += dO^T P;
+//  * wave g + 4 keeps V: dP = dO V^T; one block later, with the partner's P of that block,
+//    dS = P (dP - D) and dK^T += Q^T dS.
+// Each wave runs two of the four products per 64-query block, and while one wave of a SIMD
+// turns scores into P or dS the other keeps the matrix unit busy.  One barrier per block: it
+// publishes the block's P and releases the buffers of the block before, which is refilled with
+// the block two ahead (three Q/dO buffers, since Q of a block is read again one block later).
+// P reaches dS rounded to bf16 (the form it takes in the dV product as well).
+// Causal problems take the role-split kernel (same-box A/B, medians, against dkdv_kernel: B=1
+// H=32 N=16384 -2.8% per backward call, B=2 H=16 N=4096 -5.7%, B=8 H=16 N=2048 -5.2%).  Without
+// the mask the compiler keeps more lane addresses live across its loop and spills at d = 128,
+// so non-causal problems keep dkdv_kernel.
+template <bool CAUSAL>
+constexpr bool kDkdvRoleSplit = CAUSAL;
+constexpr int kSplitWaves = 8;
+constexpr int kSplitThreads = 64 * kSplitWaves;
+constexpr int kPexBytes = 2 * 4 * 4096;  // 2 blocks x 4 key groups x (4 x 64 lanes x 16 bytes)
+template <int D>
+constexpr int kDkdvSplitLds = 6 * Geo<D>::kTile + kRowValsBytes + kPexBytes;
+
+template <int D>
+__device__ __forceinline__ int query_of(int tt, int i, int hf) {  // query row of score i, tile tt
+  return 32 * tt + 8 * (i >> 2) + 4 * hf + (i & 3);
+}
+
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kSplitThreads, kSplitThreads), amdgpu_waves_per_eu(2, 2)))
+void dkdv_split_kernel(BwdParams p) {
+  using G = Geo<D, kSplitWaves>;
+  constexpr int kDT = D / 32;
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, ln = lane & 31, hf = lane >> 5;
+  const int kg = wave & 3, role = wave >> 2;  // role 0 keeps K (P, dV), role 1 keeps V (dS, dK)
+  const int BH = p.BH, Nq = p.Nq, Nk = p.Nk, kshift = Nk - Nq;
+  // ascending kb is heaviest first (causal), as in dkdv_kernel
+  const int bh = blockIdx.x % BH, kb = blockIdx.x / BH;
+  const int tile_key0 = kb * kRows;
+  const int my_key = tile_key0 + kg * 32 + ln;
+  const int b = bh / p.H, h = bh - b * p.H;
+
+  bf16x8 kvf[D / 16];
+  if (role == 0)
+    load_rows<D>(p.k + b * p.sk.b + h * p.sk.h, p.sk.n, my_key, Nk, hf, p.negate, kvf);
+  else
+    load_rows<D>(p.v + b * p.sv.b + h * p.sv.h, p.sv.n, my_key, Nk, hf, 0, kvf);
+  f32x16 acc[kDT];  // dV^T (role 0) or dK^T (role 1) of this lane's key
+#pragma unroll
+  for (int t = 0; t < kDT; ++t) acc[t] = (f32x16){};
+
+  const int n_qb = (Nq + kBlk - 1) / kBlk;
+  int jb = 0;
+  if (CAUSAL) jb = max(0, tile_key0 - kshift) / kBlk;
+  const __bf16* qh = p.q + b * p.sq.b + h * p.sq.h;
+  const __bf16* doh = p.dO + b * p.sdo.b + h * p.sdo.h;
+  const unsigned qsb = (unsigned)(p.sq.n * 2), dosb = (unsigned)(p.sdo.n * 2);
+  const float* lh = p.lse2 + (int64_t)bh * Nq;
+  const float* dh = p.dd + (int64_t)bh * Nq;
+  const unsigned base = (unsigned)(uintptr_t)(lds_void*)smem;
+  // LDS: buffer u (0..2) holds Q at 2u kTile and dO at (2u + 1) kTile; then the rows' LSE2 and D
+  // (512 bytes per buffer); then P of two blocks, per key group 4 slices x 64 lanes x 16 bytes.
+  char* rowvals = smem + 6 * G::kTile;
+  char* pex = rowvals + kRowValsBytes;
+  auto load_block = [&](int jq, int buf) {
+    const int limit = Nq - 1 - jq * kBlk;
+    dma_tile<D, kSplitWaves>(qh + (int64_t)jq * kBlk * p.sq.n, smem + 2 * buf * G::kTile, wave, lane, limit, qsb);
+    dma_tile<D, kSplitWaves>(doh + (int64_t)jq * kBlk * p.sdo.n, smem + (2 * buf + 1) * G::kTile, wave, lane, limit,
+                             dosb);
+    // the rows' LSE2 (wave 5) and D (wave 6): role-1 waves, which have less arithmetic
+    if (wave == 5 || wave == 6) {
+      const int r = lane < limit ? lane : limit;
+      const float* src = (wave == 5 ? lh : dh) + (int64_t)jq * kBlk + r;
+      __builtin_amdgcn_global_load_lds((global_cvoid*)src, (lds_void*)(rowvals + buf * 512 + (wave - 5) * 256), 4, 0,
+                                       0);
+    }
+  };
+  if (jb < n_qb) {
+    load_block(jb, 0);
+    if (jb + 1 < n_qb) load_block(jb + 1, 1);
+    wait_vmcnt<0>();
+    __syncthreads();
+  }
+  const float c = p.c_log2;
+  f32x16 dpp[2];  // role 1: dP of the block before
+  // role 1, for the block in buffer ub whose P sits in exchange slot par: dS and dK^T += Q^T dS
+  // role 1, for the block in buffer ub whose P sits in exchange slot par: dS = P (dP - D) and
+  // dK^T += Q^T dS, tile by tile; with `next` >= 0 the dP chain of the following block (dO in
+  // buffer next) goes out after each tile's dK slices, into that tile's dP registers.
+  // LDS operand addresses: this lane's part for buffer 0, computed once; a buffer's are these
+  // plus its offset (one add per register), the 32-row tile an immediate offset.
+  LaneAddrs<D> la;
+  la.init(base, lane);
+  auto ds_dk = [&](int ub, int par, int next) {
+    const bf16x8* pr = (const bf16x8*)(pex + (par * 4 + kg) * 4096);
+    const float* dvals = (const float*)(rowvals + ub * 512 + 256);
+    LaneAddrs<D> aq, ado;
+    aq.shift(la, (unsigned)(2 * ub * G::kTile));
+    if (next >= 0) ado.shift(la, (unsigned)((2 * next + 1) * G::kTile));
+    bf16x8 dsb[4];
+    auto tile_ds = [&]<int TT>(IC<TT>) {
+      const bf16x8 p0 = pr[(2 * TT) * 64 + lane], p1 = pr[(2 * TT + 1) * 64 + lane];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float pv = (float)(i < 8 ? p0[i & 7] : p1[i & 7]);
+        dsb[2 * TT + (i >> 3)][i & 7] = (__bf16)(pv * (dpp[TT][i] - dvals[query_of<D>(TT, i, hf)]));
+      }
+      tp_step<D>(aq.tr, dsb, acc, 2 * TT, IC<2 * TT>{});  // dK^T += Q^T dS
+      tp_step<D>(aq.tr, dsb, acc, 2 * TT + 1, IC<2 * TT + 1>{});
+      if (next >= 0) {  // dP = dO V^T of the next block, tile TT
+        bf16x8 a[D / 16];
+        issue_rows<D, 32 * TT * D * 2>(ado.row, a);
+        rows_product<D, 0>(a, kvf, dpp[TT]);
+      }
+    };
+    tile_ds(IC<0>{});
+    tile_ds(IC<1>{});
+  };
+  // The role is fixed per wave, so each role runs its own copy of the block loop (same barriers):
+  // values one role carries across blocks then take no registers in the other's code.
+  if (role == 0) {
+    for (int jq = jb; jq < n_qb; ++jq) {
+      const int u = (jq - jb) % 3, up = u == 0 ? 2 : u - 1;
+      const int par = (jq - jb) & 1;
+      const int q0 = jq * kBlk;
+      const bool masked = (CAUSAL && q0 + kshift < tile_key0 + kRows - 1) || q0 + kBlk > Nq;
+      // S of both 32-query tiles first (independent chains), then per tile: P, its half of the
+      // exchange, and its two dV^T slices, so that tile 1's exponentials run beside tile 0's MFMAs.
+      LaneAddrs<D> aq, ado;
+      aq.shift(la, (unsigned)(2 * u * G::kTile));
+      ado.shift(la, (unsigned)((2 * u + 1) * G::kTile));
+      f32x16 sc[2];
+      {
+        bf16x8 a[D / 16];  // S = Q K^T, tile 0 then tile 1
+        issue_rows<D, 0>(aq.row, a);
+        rows_product<D, 0>(a, kvf, sc[0]);
+        issue_rows<D, 32 * D * 2>(aq.row, a);
+        rows_product<D, 0>(a, kvf, sc[1]);
+      }
+      const float* lv = (const float*)(rowvals + u * 512);
+      bf16x8* pw = (bf16x8*)(pex + (par * 4 + kg) * 4096);
+      bf16x8 pb[4];
+      auto tile_p = [&]<int TT>(IC<TT>) {
+        if (masked) {  // hidden scores get -inf (P = 0)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qg = q0 + query_of<D>(TT, i, hf);
+            const bool vis = qg < Nq && (!CAUSAL || my_key <= qg + kshift);
+            sc[TT][i] = vis ? sc[TT][i] : -__builtin_inff();
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          pb[2 * TT + (i >> 3)][i & 7] =
+              (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[TT][i], c, -lv[query_of<D>(TT, i, hf)]));
+        pw[(2 * TT) * 64 + lane] = pb[2 * TT];
+        pw[(2 * TT + 1) * 64 + lane] = pb[2 * TT + 1];
+        tp_step<D>(ado.tr, pb, acc, 2 * TT, IC<2 * TT>{});  // dV^T += dO^T P
+        tp_step<D>(ado.tr, pb, acc, 2 * TT + 1, IC<2 * TT + 1>{});
+      };
+      tile_p(IC<0>{});
+      tile_p(IC<1>{});
+      wait_vmcnt<0>();
+      __syncthreads();  // P of block jq is in LDS; block jq + 1 has landed; block jq - 1 is done with
+      if (jq + 2 < n_qb) load_block(jq + 2, up);
+    }
+  } else {
+    for (int jq = jb; jq < n_qb; ++jq) {
+      const int u = (jq - jb) % 3, up = u == 0 ? 2 : u - 1;
+      const int par = (jq - jb) & 1;
+      if (jq > jb) {
+        ds_dk(up, par ^ 1, u);  // block jq - 1, then dP = dO V^T of block jq
+      } else {
+        LaneAddrs<D> ado;
+        ado.shift(la, (unsigned)((2 * u + 1) * G::kTile));
+        bf16x8 a[D / 16];
+        issue_rows<D, 0>(ado.row, a);
+        rows_product<D, 0>(a, kvf, dpp[0]);
+        issue_rows<D, 32 * D * 2>(ado.row, a);
+        rows_product<D, 0>(a, kvf, dpp[1]);
+      }
+      wait_vmcnt<0>();
+      __syncthreads();  // (the partner's side of the same barrier)
+      if (jq + 2 < n_qb) load_block(jq + 2, up);
+    }
+    if (jb < n_qb) ds_dk((n_qb - 1 - jb) % 3, (n_qb - 1 - jb) & 1, -1);
+  }
+  wait_vmcnt<0>();
+  if (my_key < Nk) {
+    if (role == 0)
+      store_row<D>(p.dv, b * p.sdv.b + h * p.sdv.h + my_key * p.sdv.n, hf, acc, 1.f, p.g_bf16);
+    else
+      store_row<D>(p.dk, b * p.sdk.b + h * p.sdk.h + my_key * p.sdk.n, hf, acc, p.scale, p.g_bf16);
+  }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch_bwd(const BwdParams& p, const void* o, Strides so, int o_bf16, const float* lse, float* dd,
                       float* lse2, hipStream_t s) {
@@ -744,7 +946,12 @@ hipError_t launch_bwd(const BwdParams& p, const void* o, Strides so, int o_bf16,
   static std::atomic<unsigned long long> done_dq4{0}, done_dq8{0}, done_dkdv{0};
   if ((e = raise_lds_limit((const void*)dq_kernel<D, CAUSAL, 4>, G::kLds, done_dq4)) != hipSuccess) return e;
   if ((e = raise_lds_limit((const void*)dq_kernel<D, CAUSAL, 8>, G::kLds, done_dq8)) != hipSuccess) return e;
-  if ((e = raise_lds_limit((const void*)dkdv_kernel<D, CAUSAL>, kDkdvLds<D>, done_dkdv)) != hipSuccess) return e;
+  if constexpr (kDkdvRoleSplit<CAUSAL>) {
+    if ((e = raise_lds_limit((const void*)dkdv_split_kernel<D, CAUSAL>, kDkdvSplitLds<D>, done_dkdv)) != hipSuccess)
+      return e;
+  } else {
+    if ((e = raise_lds_limit((const void*)dkdv_kernel<D, CAUSAL>, kDkdvLds<D>, done_dkdv)) != hipSuccess) return e;
+  }
   const int64_t rows = (int64_t)p.BH * p.Nq;
   constexpr int rpb = 64 / (D / 4);
   hipLaunchKernelGGL(row_dot_kernel<D>, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(64), 0, s, p.dO, p.sdo, o, so,
@@ -762,7 +969,10 @@ hipError_t launch_bwd(const BwdParams& p, const void* o, Strides so, int o_bf16,
     hipLaunchKernelGGL((dq_kernel<D, CAUSAL, 4>), dim3(gq), dim3(kThreads), G::kLds, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(gk), dim3(kThreads), kDkdvLds<D>, s, p);
+  if constexpr (kDkdvRoleSplit<CAUSAL>)
+    hipLaunchKernelGGL((dkdv_split_kernel<D, CAUSAL>), dim3(gk), dim3(kSplitThreads), kDkdvSplitLds<D>, s, p);
+  else
+    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL>), dim3(gk), dim3(kThreads), kDkdvLds<D>, s, p);
   return hipGetLastError();
 }
 

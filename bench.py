@@ -23,8 +23,9 @@ compulsory bytes (the input read once, the output and the row LSE written once).
 
 Besides the driver's fields, `roofline` and `cpu_baseline`, the line carries `provenance` (source
 hashes, git commit where available, GPU, ROCm/HIP/torch versions, seed); on the attention legs
-`clock`, the sustained engine clock measured on the GPU by mifa_clock_probe during a further
-second of untimed launches after the timed ones, and the percentage of the peak at that clock; and on the forward
+`clock`, the sustained engine clock measured on the GPU by short mifa_clock_probe runs during a
+further second of untimed launches after the timed ones, and the percentage of the peak at that
+clock; and on the forward
 legs `parity`, the errors of the last timed launch's O and LSE on the rows the CPU-baseline leg
 computed with the float64 oracle.
 """
@@ -160,55 +161,61 @@ def host_info() -> dict:
 
 PEAK_CLOCK_MHZ = 2400.0    # MI355X peak engine clock, the clock the 2.5 PFLOP/s figure assumes
 CLOCK_WINDOW_S = 1.0       # untimed launches after the timed steps, during which the clock is measured
-CLOCK_SETTLE_S = 0.25      # into that window, when the clock probe starts
-CLOCK_SPAN_US = 500_000    # the probe's span
+CLOCK_SETTLE_S = 0.25      # into that window, when the first clock probe starts
+CLOCK_SPAN_US = 20         # each probe's span: short, since a probe wave holds a slot on its CU
+CLOCK_PROBE_GAP_S = 0.015  # at least this long between two probes
+CLOCK_MAX_PROBES = 40
 
 
 def sample_clock(step, value_tflops):
     """The sustained engine clock under this workload, measured on the GPU.  After the timed
     region (untimed, not part of `value`) the same step keeps running for CLOCK_WINDOW_S
-    seconds; CLOCK_SETTLE_S into that window mifa_clock_probe starts 8 single-wave probes on a
-    second stream, which read the shader-clock and real-time counters CLOCK_SPAN_US apart.
-    Returns the per-probe clocks and, for a compute-bound leg, the bf16 peak scaled to their
-    median and `value_tflops` as a percentage of it."""
+    seconds; from CLOCK_SETTLE_S on, every CLOCK_PROBE_GAP_S or more, mifa_clock_probe runs 8
+    single-wave probes on a second stream that read the shader-clock and real-time counters
+    CLOCK_SPAN_US apart.  Short probes: a kernel that fills every CU's registers cannot place a
+    workgroup beside a probe wave, so a long probe would take CUs away from the workload it
+    measures (a 20 us probe every 15 ms or more holds 8 CUs for well under 1% of the window).
+    Returns the median over all probes and, for a compute-bound leg, the bf16 peak scaled to it
+    and `value_tflops` as a percentage of it."""
     import torch
 
     from io_aware_softmax_mifa_amd import binding
 
-    out = {"source": (f"mifa_clock_probe: 8 single-wave probes on a second stream read s_memtime and "
-                      f"s_memrealtime {CLOCK_SPAN_US / 1e3:g} ms apart, starting {CLOCK_SETTLE_S:g} s into "
-                      f"{CLOCK_WINDOW_S:g} s of further launches of the same step after the timed steps"),
-           "probe_mhz": None, "median_mhz": None, "min_mhz": None, "max_mhz": None, "error": None}
-    buf = torch.zeros(32, dtype=torch.int64, device="cuda")
+    out = {"source": (f"mifa_clock_probe: groups of 8 single-wave probes on a second stream, each reading "
+                      f"s_memtime and s_memrealtime {CLOCK_SPAN_US} us apart, one group every "
+                      f">= {CLOCK_PROBE_GAP_S * 1e3:g} ms from {CLOCK_SETTLE_S:g} s into {CLOCK_WINDOW_S:g} s of "
+                      f"further launches of the same step after the timed steps"),
+           "probes": 0, "median_mhz": None, "min_mhz": None, "max_mhz": None, "error": None}
+    buf = torch.zeros(CLOCK_MAX_PROBES * 32, dtype=torch.int64, device="cuda")
     side = torch.cuda.Stream()  # default priority; non-blocking with respect to the null stream
-    khz, launched, prev = 0, None, None
+    khz, n, last, prev = 0, 0, None, None
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < CLOCK_WINDOW_S:
-        for _ in range(20):
+        for _ in range(5):
             step()
         ev = torch.cuda.Event()
         ev.record()
         if prev is not None:
-            prev.synchronize()  # keep about one chunk queued behind the running one
+            prev.synchronize()  # keep about one group of steps queued behind the running one
         prev = ev
-        if launched is None and time.perf_counter() - t0 >= CLOCK_SETTLE_S:
-            st, khz = binding.mifa_clock_probe_raw(buf, CLOCK_SPAN_US, side.cuda_stream)
-            launched = time.perf_counter() - t0
+        now = time.perf_counter() - t0
+        if (now >= CLOCK_SETTLE_S and n < CLOCK_MAX_PROBES and (last is None or now - last >= CLOCK_PROBE_GAP_S)
+                and now + 2 * CLOCK_PROBE_GAP_S < CLOCK_WINDOW_S):
+            st, khz = binding.mifa_clock_probe_raw(buf[32 * n:], CLOCK_SPAN_US, side.cuda_stream)
             if st != 0:
                 out["error"] = f"mifa_clock_probe: {binding.mifa_status_string(st)}"
                 break
+            n, last = n + 1, now
     torch.cuda.synchronize()
-    if out["error"] is None and launched is None:
-        out["error"] = "the probe was not launched"
-    if out["error"] is None and CLOCK_WINDOW_S - launched < CLOCK_SPAN_US * 1e-6:
-        out["error"] = "the step stopped before the probe's span ended"
+    out["probes"] = n
+    if out["error"] is None and n == 0:
+        out["error"] = "no probe was launched"
     if out["error"] is None:
-        v = buf.cpu().tolist()
+        v = buf[:32 * n].cpu().tolist()
         mhz = []
-        for w in range(8):
+        for w in range(8 * n):
             dt, dr = v[4 * w + 2] - v[4 * w], v[4 * w + 3] - v[4 * w + 1]
             mhz.append(dt / dr * khz / 1e3 if dr > 0 else float("nan"))
-        out["probe_mhz"] = [round(x, 1) for x in mhz]
         if not all(100.0 < x < 3000.0 for x in mhz):
             out["error"] = "probe clock outside 100..3000 MHz"
         else:
@@ -249,7 +256,7 @@ def provenance(seed) -> dict:
     except OSError:
         pass
     props = torch.cuda.get_device_properties(0)
-    name = None
+    name, name_err = None, None
     try:
         import amdsmi
 
@@ -258,17 +265,20 @@ def provenance(seed) -> dict:
             handles = amdsmi.amdsmi_get_processor_handles()
             if handles:
                 name = amdsmi.amdsmi_get_gpu_asic_info(handles[0]).get("market_name") or None
+                if not name:
+                    name = amdsmi.amdsmi_get_gpu_board_info(handles[0]).get("product_name") or None
         finally:
             amdsmi.amdsmi_shut_down()
-    except Exception:  # noqa: BLE001 -- the name is informational
-        name = None
+    except Exception as e:  # noqa: BLE001 -- the name is informational
+        name, name_err = None, repr(e)[:200]
     name = name or torch.cuda.get_device_name(0) or None
     from io_aware_softmax_mifa_amd import binding
 
     return {"git_sha": sha, "sources_sha256": h.hexdigest()[:16], "gpu_name": name,
             "gpu_arch": getattr(props, "gcnArchName", None), "cus": props.multi_processor_count,
             "rocm_version": rocm, "hip_runtime": torch.version.hip, "torch_version": torch.__version__,
-            "library": binding.mifa_version(), "seed": seed}
+            "library": binding.mifa_version(), "seed": seed,
+            **({"gpu_name_note": f"amdsmi: {name_err}; HIP device name used"} if name_err else {})}
 
 
 def event_stats(starts, ends) -> dict:

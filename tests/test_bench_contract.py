@@ -49,7 +49,7 @@ def test_json_line(workload):
         assert d["metric"].startswith("attention fwd TFLOP/s (bf16, causal)")
         ck = d["clock"]
         assert ck["error"] is None, ck
-        assert len(ck["probe_mhz"]) == 8 and 100 < ck["min_mhz"] <= ck["median_mhz"] <= ck["max_mhz"] < 3000
+        assert ck["probes"] >= 1 and 100 < ck["min_mhz"] <= ck["median_mhz"] <= ck["max_mhz"] < 3000
         assert ck["clock_adjusted_peak_tflops"] == pytest.approx(2500.0 * ck["median_mhz"] / 2400.0)
 
 

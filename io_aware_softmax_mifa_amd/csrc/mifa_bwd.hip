@@ -761,8 +761,9 @@ constexpr int kPexBytes = 2 * 4 * 4096;  // 2 blocks x 4 key groups x (4 x 64 la
 template <int D>
 constexpr int kDkdvSplitLds = 6 * Geo<D>::kTile + kRowValsBytes + kPexBytes;
 
-template <int D>
-__device__ __forceinline__ int query_of(int tt, int i, int hf) {  // query row of score i, tile tt
+// Query row (within a 64-query block) of accumulator element i of 32-query tile tt, for the lane
+// half hf: the row order of a 32x32 accumulator.
+__device__ __forceinline__ int query_of(int tt, int i, int hf) {
   return 32 * tt + 8 * (i >> 2) + 4 * hf + (i & 3);
 }
 
@@ -846,7 +847,7 @@ void dkdv_split_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float pv = (float)(i < 8 ? p0[i & 7] : p1[i & 7]);
-        dsb[2 * TT + (i >> 3)][i & 7] = (__bf16)(pv * (dpp[TT][i] - dvals[query_of<D>(TT, i, hf)]));
+        dsb[2 * TT + (i >> 3)][i & 7] = (__bf16)(pv * (dpp[TT][i] - dvals[query_of(TT, i, hf)]));
       }
       tp_step<D>(aq.tr, dsb, acc, 2 * TT, IC<2 * TT>{});  // dK^T += Q^T dS
       tp_step<D>(aq.tr, dsb, acc, 2 * TT + 1, IC<2 * TT + 1>{});
@@ -887,7 +888,7 @@ void dkdv_split_kernel(BwdParams p) {
         if (masked) {  // hidden scores get -inf (P = 0)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int qg = q0 + query_of<D>(TT, i, hf);
+            const int qg = q0 + query_of(TT, i, hf);
             const bool vis = qg < Nq && (!CAUSAL || my_key <= qg + kshift);
             sc[TT][i] = vis ? sc[TT][i] : -__builtin_inff();
           }
@@ -895,7 +896,7 @@ void dkdv_split_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           pb[2 * TT + (i >> 3)][i & 7] =
-              (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[TT][i], c, -lv[query_of<D>(TT, i, hf)]));
+              (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sc[TT][i], c, -lv[query_of(TT, i, hf)]));
         pw[(2 * TT) * 64 + lane] = pb[2 * TT];
         pw[(2 * TT + 1) * 64 + lane] = pb[2 * TT + 1];
         tp_step<D>(ado.tr, pb, acc, 2 * TT, IC<2 * TT>{});  // dV^T += dO^T P

@@ -183,3 +183,21 @@ def test_strided_bf16_long_launch_shape(d):
     for h in (0, 21, H - 1):
         ro, rl = attention_fp64(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], causal=True, scale=scale)
         check_o(o[:, h:h + 1], lse[:, h:h + 1], ro, rl, f"strided bf16 long d={d} head {h}", True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_strided_bf16_key_split_pairs(d):
+    """[B, N, H, d] storage with bf16 O through the key-split launch over tile pairs (causal,
+    Nq > 1024, between 256 and 512 query tiles of 128 rows), rectangular: 24 heads of 1,500
+    queries against 1,700 keys (288 tiles).  Three heads against the oracle."""
+    from io_aware_softmax_mifa_amd import binding
+
+    B, H, Nq, Nk = 1, 24, 1500, 1700
+    (q, k, v), (gq, gk, gv) = bnhd_views(B, H, Nq, Nk, d, 430 + d)
+    scale = W.fp32_scale(d)
+    out = torch.empty((B, Nq, H, d), dtype=torch.bfloat16, device="cuda").transpose(1, 2)
+    o, lse = binding.attention(gq, gk, gv, causal=True, scale=scale, out=out)
+    torch.cuda.synchronize()
+    for h in (0, 11, H - 1):
+        ro, rl = attention_fp64(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], causal=True, scale=scale)
+        check_o(o[:, h:h + 1], lse[:, h:h + 1], ro, rl, f"strided bf16 key-split pairs d={d} head {h}", True)

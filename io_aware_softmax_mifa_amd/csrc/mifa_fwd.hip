@@ -429,7 +429,7 @@ struct FwdParams {
 // O and LSE stores.
 template <typename C, bool CAUSAL>
 __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int split) {
-  constexpr int D = C::D, BC = C::BC, NBUF = C::NBUF, kBR = C::kBR;
+  constexpr int BC = C::BC, NBUF = C::NBUF, kBR = C::kBR;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -845,6 +845,12 @@ hipError_t dispatch(const Problem& pr, hipStream_t stream) {
   const int64_t big_tiles = (int64_t)pr.BH * ((pr.Nq + 255) / 256);
   const int64_t tiles = (int64_t)pr.BH * ((pr.Nq + 127) / 128);
   if (pr.n_splits == 1 && pr.Nq > kLongN && big_tiles > kCUs) return launch<Cfg<D, 64, 8, 4>, CAUSAL>(pr, stream);
+  // Without the mask every tile is equally heavy, so exactly one 256-row tile per CU already
+  // fills the GPU evenly: 8 waves there too (same-box A/B, medians, against 4-wave workgroups:
+  // B=1 H=8 N=8192 d=128 -8%, B=1 H=4 N=16384 -8%, B=1 H=16 N=4096 d=64 -11%, B=4 H=16 N=1024
+  // d=128 -6%).
+  if (!CAUSAL && pr.n_splits == 1 && pr.Nq >= kLongN && big_tiles >= kCUs)
+    return launch<Cfg<D, 64, 8, 4>, CAUSAL>(pr, stream);
   // Few 128-row tiles (at most one per CU) over at least 512 keys: two groups of four waves per
   // tile split the key blocks, so twice as many waves share the work of a tile.  Measured on
   // MI355X (same-box A/B, medians): B=4 H=8 N=1024 d=64 -8% causal and non-causal against one

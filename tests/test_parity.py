@@ -131,6 +131,19 @@ def test_long_sequence_launch_shape(d, causal, dist):
           f"long d={d} causal={causal} {dist} sampled rows")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_non_causal_one_tile_per_cu(d):
+    """Without the mask, exactly 256 query tiles of 256 rows take the 8-wave launch: B=4 H=16
+    N=1024, and B=2 H=16 N=2000 (partial last tile); every row of every head checked."""
+    for B, H, N in ((4, 16, 1024), (2, 16, 2000)):
+        q, k, v = W.make_inputs(B, H, N, d, seed=5300 + N + d)
+        scale = W.fp32_scale(d)
+        say(f"non-causal, 256 tiles: B={B} H={H} N={N} d={d}")
+        o, lse = run_gpu(q, k, v, False, scale, poison=True)
+        ro, rl = attention_fp64(q, k, v, causal=False, scale=scale)
+        check(o, lse, ro, rl, f"non-causal 256 tiles N={N} d={d}")
+
+
 # ---- the key-split launch (few tiles: two wave groups per tile share the key blocks) --------
 
 @pytest.mark.parametrize("d", [64, 128])

@@ -959,9 +959,12 @@ hipError_t launch_bwd(const BwdParams& p, const void* o, Strides so, int o_bf16,
                      o_bf16, lse, dd, lse2, p.H, p.Nq, rows);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 8-wave dq workgroups for long sequences with at least one such workgroup per CU
+  // 8-wave dq workgroups for long sequences with more than one such workgroup per CU (causal:
+  // with exactly one per CU, nothing evens out the unequal causal tiles, and 4-wave workgroups,
+  // two per CU, are faster: B=1 H=8 N=8192 and B=1 H=4 N=16384 -10% per backward call in a
+  // same-box A/B); without the mask one per CU suffices.
   const int64_t big_q = (int64_t)p.BH * ((p.Nq + 255) / 256);
-  const bool dq8 = p.Nq > 4096 && big_q >= 256;
+  const bool dq8 = CAUSAL ? (p.Nq > 4096 && big_q > 256) : (p.Nq >= 4096 && big_q >= 256);
   const unsigned gq = (unsigned)(dq8 ? big_q : (int64_t)p.BH * ((p.Nq + kRows - 1) / kRows));
   const unsigned gk = (unsigned)((int64_t)p.BH * ((p.Nk + kRows - 1) / kRows));
   if (dq8)

@@ -95,6 +95,7 @@ SHAPES = [
     (1, 2, 64, 64, 64, True, 16),        # exactly one block: the pipeline's prologue and epilogue only
     (1, 1, 4096, 4096, 64, True, 17),    # up to 64 blocks per key tile: the ring wraps many times
     (1, 16, 4160, 4160, 64, True, 18),   # 272 long dq tiles: the 8-wave dq kernel and its 4-buffer ring
+    (1, 16, 4096, 4096, 64, False, 19),  # no mask, exactly 256 long dq tiles: the 8-wave dq kernel
 ]
 
 

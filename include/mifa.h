@@ -273,7 +273,9 @@ int mifa_softmax_rows(const void* x, void* y, float* lse, int64_t rows, int64_t 
  * (s_memtime, one count per engine-clock cycle) and the fixed-rate real-time counter
  * (s_memrealtime) at its start, sleeps for span_us microseconds of real time, and reads both
  * again.  Launch it on a second stream while the work to be measured keeps the GPU busy on
- * another; the mean engine clock of probe w in MHz is
+ * another, with a short span (tens of microseconds) repeated as often as needed: a probe wave
+ * holds a slot on its CU for the whole span, and a kernel that fills every CU's register file
+ * cannot place a workgroup beside it.  The mean engine clock of probe w in MHz is
  *     (out[4w+2] - out[4w+0]) / (out[4w+3] - out[4w+1]) * realtime_khz / 1000.
  *   out          device pointer to 32 int64 values (8-byte aligned), overwritten when the
  *                kernel has run: {memtime start, realtime start, memtime end, realtime end}

@@ -23,8 +23,8 @@
 //    every two blocks and each DMA has two block-times to land.
 //  * Long sequences use 8-wave workgroups (one per CU, 128 KB of LDS): every K/V block brought
 //    into LDS then serves 256 query rows, which halves the L2->LDS stream; shorter ones use
-//    4-wave workgroups (two per CU), whose tiles are shorter and which fill the 256 CUs more
-//    evenly.
+//    4-wave workgroups (two per CU, three at d = 64), whose tiles are shorter and which fill the
+//    256 CUs more evenly.
 //  * Scores are computed transposed, S^T = K Q^T, on MFMA.  In the 32x32 accumulator layout a
 //    lane then holds 16 scores of ONE query (its lane % 32), so the row max and row sum are
 //    in-lane reductions plus one v_permlane32_swap with the other half of the wave.
@@ -193,8 +193,12 @@ __device__ __forceinline__ void issue_one(const __bf16* __restrict__ base, char*
 template <typename C, bool CAUSAL>
 struct Wave {
   static constexpr int D = C::D, BC = C::BC;
-  static constexpr int kKR = 6;    // K operand ring depth (S^T reads run kKR-1 MFMAs ahead)
-  static constexpr int kVLook = 8; // V^T reads run kVLook PV steps ahead
+  // Operand ring depths.  K operand reads run kKR-1 MFMAs ahead, V^T reads kVLook PV steps.  At
+  // d = 64 the shallower rings keep a wave within 168 registers, so that three waves fit on a
+  // SIMD (the 4-wave launch then holds three workgroups per CU): same results, 1-2% faster on
+  // B=4 H=8 N=1024 and 11% on B=16 H=16 N=512 causal (1,024 four-wave workgroups), same-box A/B.
+  static constexpr int kKR = D == 64 ? 4 : 6;
+  static constexpr int kVLook = D == 64 ? 3 : 8;
   static constexpr int kVR = 2 * (kVLook + 1);
 
   bf16x8 qf[C::kDS];
@@ -732,8 +736,13 @@ __device__ __forceinline__ void fwd_tile(const FwdParams& p, int bh, int qt, int
   }
 }
 
+// Register budget: two waves per SIMD (256 registers each), three at d = 64 (168 each).
+template <typename C>
+constexpr int kWavesPerSimd = C::D == 64 ? 3 : 2;
+
 template <typename C, bool CAUSAL, bool PAIR>
-__global__ __attribute__((amdgpu_flat_work_group_size(C::kThreads, C::kThreads), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(C::kThreads, C::kThreads),
+                          amdgpu_waves_per_eu(kWavesPerSimd<C>, kWavesPerSimd<C>)))
 void mifa_fwd_kernel(FwdParams p) {
   const int BH = p.BH, n_qtiles = p.n_qtiles;
   // ---- which (key range, b*H + h, q-tile) this workgroup owns ----
@@ -835,7 +844,7 @@ hipError_t launch(const Problem& pr, hipStream_t stream, bool pair_tiles = true)
 
 // Launch-shape choice: 8-wave workgroups (256 rows, one per CU) for sequences longer than 1024
 // with more of them than CUs; 8-wave workgroups with two key-split groups (128 rows) for few
-// tiles; otherwise 4-wave workgroups (128 rows, two per CU).  Measured on
+// tiles; otherwise 4-wave workgroups (128 rows, two per CU; three at d = 64).  Measured on
 // MI355X (same-box A/B): with 8 waves B=1 H=32 N=16384 causal runs ~8 % faster, B=2 H=16
 // N=4096 causal ~7 % and B=8 H=16 N=2048 causal ~3 %; with exactly one 256-row tile per CU
 // (B=1 H=4 N=16384, B=1 H=8 N=8192) 4 waves are 1-2.5 % faster, since two workgroups per CU

@@ -1,6 +1,7 @@
 """Register budget of the built kernels, read from the AMDGPU metadata of libmifa.so's own device
 code: no kernel spills vector registers or uses scratch memory, and the forward kernels stay within the 256 vector
-registers per lane that two waves per SIMD leave each wave (the launch shapes assume it)."""
+registers per lane that two waves per SIMD leave each wave, the d = 64 ones within the 168 of three
+(the launch shapes assume it)."""
 import os
 import re
 import shutil
@@ -64,3 +65,5 @@ def test_no_spills_and_forward_register_budget(tmp_path):
         assert m.get("vgpr_spill_count", 0) == 0, (name, m)
     for name in fwd:
         assert ks[name]["vgpr_count"] <= 256, (name, ks[name])
+        if "CfgILi64E" in name:  # d = 64: three waves per SIMD (512 / 3, in granules of 8)
+            assert ks[name]["vgpr_count"] <= 168, (name, ks[name])

@@ -144,6 +144,20 @@ def test_non_causal_one_tile_per_cu(d):
         check(o, lse, ro, rl, f"non-causal 256 tiles N={N} d={d}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_d64_three_workgroups_per_cu(causal):
+    """d = 64 with many 128-row tiles and N <= 1024 takes the 4-wave launch, three workgroups
+    resident per CU (three waves per SIMD): 1,024 tiles causal, 640 with a ragged last tile
+    non-causal; every row of every head checked."""
+    B, H, N = (16, 16, 512) if causal else (8, 16, 600)
+    q, k, v = W.make_inputs(B, H, N, 64, seed=5400 + N)
+    scale = W.fp32_scale(64)
+    say(f"d=64 4-wave, three per CU: B={B} H={H} N={N} causal={causal}")
+    o, lse = run_gpu(q, k, v, causal, scale, poison=True)
+    ro, rl = attention_fp64(q, k, v, causal=causal, scale=scale)
+    check(o, lse, ro, rl, f"d=64 three per CU N={N} causal={causal}")
+
+
 # ---- the key-split launch (few tiles: two wave groups per tile share the key blocks) --------
 
 @pytest.mark.parametrize("d", [64, 128])

@@ -21,6 +21,10 @@ O and LSE written once).
 step is one launch over a [rows, cols] matrix, and the metric is HBM throughput of the
 compulsory bytes (the input read once, the output and the row LSE written once).
 
+`--workload GEMM-ref` times the vendor library's bf16 GEMM (torch.matmul, M = N = K = 8192) with
+its sustained clock, for context: what a plain contraction reaches on the same GPU.  It is not
+this library's code and has no CPU baseline.
+
 Besides the driver's fields, `roofline` and `cpu_baseline`, the line carries `provenance` (source
 hashes, git commit where available, GPU, ROCm/HIP/torch versions, seed); on the attention legs
 `clock`, the sustained engine clock measured on the GPU by short mifa_clock_probe runs during a
@@ -680,6 +684,68 @@ def bench_backward(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_gemm_reference(args):
+    """Context leg, not this library's code: the vendor library's dense bf16 GEMM
+    (`torch.matmul`, hipBLASLt on ROCm) at M = N = K = 8192 with its sustained clock, i.e. what a
+    plain contraction with no softmax between its products reaches on this GPU.  The attention
+    legs' fractions of the 2.5 PFLOP/s peak read against it."""
+    import torch
+
+    M = N = K = 8192
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator().manual_seed(11)
+    a = torch.randn(M, K, generator=g).to(dev, torch.bfloat16)
+    b = torch.randn(K, N, generator=g).to(dev, torch.bfloat16)
+    c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        torch.matmul(a, b, out=c)
+
+    args.warmup = warm_up(step, args.warmup)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    call_ms = sum(x.elapsed_time(y) for x, y in zip(starts, ends)) / args.steps
+    f = 2.0 * M * N * K
+    value = f / (ms_per_step * 1e-3) / 1e12
+    achieved = f / (call_ms * 1e-3) / 1e12
+    log(f"timed {args.steps} GEMMs: {ms_per_step:.4f} ms/step wall, {call_ms:.4f} ms/call (HIP events)")
+    out = {
+        "metric": "bf16 GEMM TFLOP/s (torch.matmul, vendor library; reference, not mifa) and % of MI355X bf16 "
+                  "MFMA peak",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 matrices)",
+        "config": {"workload": f"GEMM-ref: C = A B, M=N=K={M}, bf16 in and out, fp32 accumulation (hipBLASLt)",
+                   "M": M, "N": N, "K": K, "flop_per_step": f, "call_ms": call_ms,
+                   "pct_of_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "cpu_baseline": None,
+    }
+    out["clock"] = sample_clock(step, value)
+    out["provenance"] = provenance(11)
+    out["config"].update(event_stats(starts, ends))
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -702,6 +768,8 @@ def main():
               "one-GPU run on that GPU's share).", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "GEMM-ref":
+        return bench_gemm_reference(args)
     if args.workload.startswith("SM"):
         return bench_softmax(args)
     if args.workload.startswith("D"):

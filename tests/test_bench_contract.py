@@ -54,6 +54,23 @@ def test_json_line(workload):
 
 
 @pytest.mark.gpu
+def test_gemm_reference_leg():
+    """The context leg: the vendor bf16 GEMM's line has the driver's fields, an MFMA roofline
+    whose fraction matches its figures, no CPU baseline, and a measured clock."""
+    r = run_bench("--workload", "GEMM-ref", "--steps", "3", "--warmup", "1")
+    print(r.stderr[-2000:], flush=True)
+    assert r.returncode == 0
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    assert KEYS <= set(d), KEYS - set(d)
+    assert d["cpu_baseline"] is None and d["value"] > 0 and "not mifa" in d["metric"]
+    rf = d["roofline"]
+    assert rf["bound"] == "mfma" and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
+    assert d["clock"]["error"] is None, d["clock"]
+
+
+@pytest.mark.gpu
 def test_cold_cache_leg():
     """--cold rotates through copies whose total exceeds twice the 256 MiB last-level cache, and a
     workload below the ridge (C2 causal, 204 FLOP/B) reports the HBM roofline in GB/s."""

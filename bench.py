@@ -22,8 +22,10 @@ step is one launch over a [rows, cols] matrix, and the metric is HBM throughput 
 compulsory bytes (the input read once, the output and the row LSE written once).
 
 `--workload GEMM-ref` times the vendor library's bf16 GEMM (torch.matmul, M = N = K = 8192) with
-its sustained clock, for context: what a plain contraction reaches on the same GPU.  It is not
-this library's code and has no CPU baseline.
+its sustained clock, for context: what a plain contraction reaches on the same GPU.  Likewise
+`--workload HBM-ref` times the runtime's 1 GiB device copy (and a 2 GiB torch.sum), the vendor's
+streaming rates the HBM-bound legs read against.  Neither is this library's code; neither has a CPU
+baseline.
 
 Besides the driver's fields, `roofline` and `cpu_baseline`, the line carries `provenance` (source
 hashes, git commit where available, GPU, ROCm/HIP/torch versions, seed); on the attention legs
@@ -746,6 +748,81 @@ def bench_gemm_reference(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_hbm_reference(args):
+    """Context leg, not this library's code: the vendor's plain streaming kernels on this GPU's
+    HBM, what the HBM-bound legs (split-KV decode, row softmax) read against.  One step = a 1 GiB
+    device copy (`copy_`, the runtime's copy kernel: 1 GiB read and 1 GiB written); `value` is its
+    rate.  Timed separately after it: a 2 GiB bf16 tensor summed (`torch.sum`, read once, fp32
+    accumulation), whose read rate goes into `config`."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    a = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1)
+    b = torch.empty_like(a)
+
+    def step():
+        b.copy_(a)
+
+    def timed(fn, steps):
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        return wall, sum(x.elapsed_time(y) for x, y in zip(starts, ends)) / steps, starts, ends
+
+    args.warmup = warm_up(step, args.warmup)
+    ms_per_step, call_ms, starts, ends = timed(step, args.steps)
+    nbytes = 2 * 2 * a.numel()
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    del a, b
+    x = torch.empty(1 << 30, dtype=torch.bfloat16, device=dev).fill_(0.5)
+    out = torch.empty((), dtype=torch.float32, device=dev)
+
+    def total():
+        torch.sum(x, dim=0, dtype=torch.float32, out=out)
+
+    for _ in range(5):
+        total()
+    _, sum_ms, _, _ = timed(total, args.steps)
+    sum_gbs = 2 * x.numel() / (sum_ms * 1e-3) / 1e9
+    log(f"timed {args.steps} copies of 2 x {nbytes // 2} bytes: {ms_per_step:.4f} ms/step wall, {call_ms:.4f} "
+        f"ms/call; sum of {2 * x.numel()} bytes: {sum_ms:.4f} ms/call")
+    out_line = {
+        "metric": "HBM GB/s of a device copy (copy_, vendor runtime; reference, not mifa) and % of MI355X HBM "
+                  "bandwidth",
+        "value": value,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (constant-filled tensors)",
+        "config": {"workload": f"HBM-ref: copy of {nbytes // 2} bytes (read and written once); then a sum of "
+                               f"{2 * x.numel()} bytes of bf16 (read once)",
+                   "bytes_per_step": nbytes, "call_ms": call_ms, "pct_of_hbm_peak": 100.0 * value / PEAK_HBM_GBS,
+                   "sum_ms": sum_ms, "sum_gbs": sum_gbs, "sum_pct_of_hbm_peak": 100.0 * sum_gbs / PEAK_HBM_GBS},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None},
+        "cpu_baseline": None,
+    }
+    out_line["provenance"] = provenance(0)
+    out_line["config"].update(event_stats(starts, ends))
+    print(json.dumps(out_line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -770,6 +847,8 @@ def main():
 
     if args.workload == "GEMM-ref":
         return bench_gemm_reference(args)
+    if args.workload == "HBM-ref":
+        return bench_hbm_reference(args)
     if args.workload.startswith("SM"):
         return bench_softmax(args)
     if args.workload.startswith("D"):

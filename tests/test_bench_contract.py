@@ -71,6 +71,22 @@ def test_gemm_reference_leg():
 
 
 @pytest.mark.gpu
+def test_hbm_reference_leg():
+    """The HBM context leg: a copy rate and a read rate, both below the 8 TB/s peak."""
+    r = run_bench("--workload", "HBM-ref", "--steps", "3", "--warmup", "1")
+    print(r.stderr[-2000:], flush=True)
+    assert r.returncode == 0
+    lines = [l for l in r.stdout.splitlines() if l.strip()]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    assert KEYS <= set(d), KEYS - set(d)
+    assert d["cpu_baseline"] is None and "not mifa" in d["metric"]
+    rf = d["roofline"]
+    assert rf["bound"] == "hbm" and 0 < rf["frac"] < 1.0 and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-9
+    assert 0 < d["config"]["sum_gbs"] < 8000.0
+
+
+@pytest.mark.gpu
 def test_cold_cache_leg():
     """--cold rotates through copies whose total exceeds twice the 256 MiB last-level cache, and a
     workload below the ridge (C2 causal, 204 FLOP/B) reports the HBM roofline in GB/s."""

@@ -161,3 +161,35 @@ def test_backward_full_size_sampled():
     got_k, got_v = pick(dk, k_rows), pick(dv, k_rows)
     rdq, rdk, rdv = attention_bwd_fp64_rows(q, k, v, do, q_rows, k_rows, causal=w.causal, scale=scale)
     check_grads((got_q, got_k, got_v), (rdq, rdk, rdv), "C4 sampled rows")
+
+
+# ---- the dq kernel's launch rule at its edges ------------------------------------------------
+# 8-wave dq workgroups (256 query rows) when causal with Nq > 4096 and more than 256 of them, or
+# without the mask with Nq >= 4096 and at least 256; 4-wave ones (128 rows) otherwise.  Each
+# case checks every gradient row of two heads (first and last) against the oracle run on those
+# heads alone (heads are independent).
+DQ_EDGES = [
+    # B, H, N, d, causal, shape
+    (1, 16, 4097, 64, True, "causal, 272 tiles of 256 rows: 8-wave dq"),
+    (1, 15, 4097, 64, True, "causal, 255 tiles of 256 rows: 4-wave dq"),
+    (1, 16, 4096, 64, False, "non-causal, exactly 256 tiles: 8-wave dq"),
+    (1, 15, 4096, 64, False, "non-causal, 240 tiles: 4-wave dq"),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,causal,shape", DQ_EDGES, ids=[c[5] for c in DQ_EDGES])
+def test_dq_launch_rule_edges(B, H, N, d, causal, shape):
+    from io_aware_softmax_mifa_amd import binding
+
+    q, k, v = W.make_inputs(B, H, N, d, seed=7100 + H + N)
+    do = W.make_grad_output(B, H, N, d, seed=7100 + H + N)
+    scale = W.fp32_scale(d)
+    say(f"B={B} H={H} N={N} d={d} causal={causal}: {shape}")
+    o, lse = binding.attention(q.cuda(), k.cuda(), v.cuda(), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    got = gpu_bwd(q, k, v, o.cpu(), lse.cpu(), do, causal, scale)
+    for h in (0, H - 1):
+        sl = (slice(0, 1), slice(h, h + 1))
+        rdq, rdk, rdv, _ = attention_bwd_fp64(q[sl], k[sl], v[sl], do[sl], causal=causal, scale=scale)
+        check_grads(tuple(g[sl] for g in got), (rdq, rdk, rdv), f"{shape}, head {h}")
+
